@@ -1,0 +1,248 @@
+"""Plain fp64 attention: the definition, the chunked running-max method, and
+the textbook gradient. TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Shapes: q, k, v, do are float arrays of shape [..., n, d] (any number of
+leading batch/head axes, identical across the four). Every computation is in
+float64. No function here blocks, fuses or reorders arithmetic beyond what
+its docstring states.
+"""
+
+import math
+
+import numpy as np
+
+
+def softmax_scale(d):
+    """The score scale 1/sqrt(d_k).
+
+    "Fast and memory-efficient exact attention 分析", section 数学表达形式:
+    scores are QK^T divided by the square root of the key dimension d_k.
+    Here d_k is the common head dimension of Q and K.
+    """
+    return 1.0 / math.sqrt(float(d))
+
+
+def _as_slices(x):
+    x = np.asarray(x, dtype=np.float64)
+    if x.ndim < 2:
+        raise ValueError("expected [..., n, d]")
+    lead = x.shape[:-2]
+    return x.reshape((int(np.prod(lead, dtype=np.int64)),) + x.shape[-2:]), lead
+
+
+def naive_fwd(q, k, v, rows=None, row_block=1024):
+    """Standard attention O = softmax(Q K^T / sqrt(d)) V, written out.
+
+    Follows the definition: "Fast and memory-efficient exact attention 分析",
+    section 数学表达形式, and "当注意力成为瓶颈…", section 平方级的诅咒
+    (S = QK^T, then a softmax over each row of S, then O = PV; each row is
+    normalised over all keys).
+
+    For every query row i:
+        s_ij = (q_i . k_j) / sqrt(d)
+        m_i  = max_j s_ij                (the textbook stable softmax: the
+                                          row max is subtracted before exp,
+                                          which leaves the softmax unchanged)
+        p_ij = exp(s_ij - m_i)
+        l_i  = sum_j p_ij
+        o_i  = (sum_j p_ij v_j) / l_i
+
+    Rows are independent by definition, so they are evaluated in blocks of
+    ``row_block`` query rows only to bound memory; ``rows`` (an index array)
+    restricts the result to those query rows. Returns (o, m, l) with
+    o: [..., r, d], m and l: [..., r] where r = number of rows evaluated.
+    """
+    q3, lead = _as_slices(q)
+    k3, _ = _as_slices(k)
+    v3, _ = _as_slices(v)
+    G, n, d = q3.shape
+    nk = k3.shape[1]
+    idx = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    r = idx.shape[0]
+    o = np.zeros((G, r, v3.shape[2]), dtype=np.float64)
+    m = np.full((G, r), -np.inf, dtype=np.float64)
+    l = np.zeros((G, r), dtype=np.float64)
+    scale = softmax_scale(d)
+    if nk == 0 or r == 0:
+        return o.reshape(lead + o.shape[1:]), m.reshape(lead + (r,)), l.reshape(lead + (r,))
+    for g in range(G):
+        for b0 in range(0, r, row_block):
+            sel = idx[b0:b0 + row_block]
+            s = (q3[g, sel, :] @ k3[g].T) * scale
+            mb = s.max(axis=1)
+            p = np.exp(s - mb[:, None])
+            lb = p.sum(axis=1)
+            o[g, b0:b0 + len(sel)] = (p @ v3[g]) / lb[:, None]
+            m[g, b0:b0 + len(sel)] = mb
+            l[g, b0:b0 + len(sel)] = lb
+    return o.reshape(lead + o.shape[1:]), m.reshape(lead + (r,)), l.reshape(lead + (r,))
+
+
+def row_stats(q, k):
+    """Per-row statistics of the softmax: m_i = max_j s_ij and
+    l_i = sum_j exp(s_ij - m_i), with s_ij = q_i . k_j / sqrt(d).
+
+    These are the running max and running sum of exponentiated scores that the
+    method keeps per query ("Self-attention Does Not Need O(n^2) Memory",
+    English digest, method bullets: a total weight accumulated with a tracked
+    maximum), taken at the end of the key sweep. Returns (m, l), each [..., n].
+    """
+    q3, lead = _as_slices(q)
+    k3, _ = _as_slices(k)
+    G, n, d = q3.shape
+    scale = softmax_scale(d)
+    m = np.empty((G, n))
+    l = np.empty((G, n))
+    for g in range(G):
+        s = (q3[g] @ k3[g].T) * scale
+        m[g] = s.max(axis=1)
+        l[g] = np.exp(s - m[g][:, None]).sum(axis=1)
+    return m.reshape(lead + (n,)), l.reshape(lead + (n,))
+
+
+def chunked_fwd(q, k, v, chunk=None):
+    """The pages' method: keys and values in chunks, a running maximum, a
+    running sum of exponentiated scores and a running weighted value sum per
+    query, divided by the sum only once at the end.
+
+    "Self-attention Does Not Need O(n^2) Memory": the abstract and the
+    method sections (方法论, 方法详解; English digest method bullets) describe
+    postponing the softmax normalisation to the end, keeping two accumulators
+    (weighted value sum and total weight) with a tracked maximum for numerical
+    stability, and splitting keys/values into chunks of about sqrt(n).
+    "当注意力成为瓶颈…", section IO感知, gives the two-block merge
+    (m = max of both block maxima; l and O combine the blocks re-based on m);
+    applying it once per chunk, in order, gives the loop below.
+
+    Starting from m = -inf, l = 0, acc = 0, for each key chunk c in order:
+        s      = q k_c^T / sqrt(d)
+        m_new  = max(m, max_j s_j)
+        alpha  = exp(m - m_new)
+        p      = exp(s - m_new)
+        l      = alpha * l + sum_j p_j
+        acc    = alpha * acc + p v_c
+        m      = m_new
+    and finally o = acc / l. ``chunk`` defaults to ceil(sqrt(n_keys)).
+    Returns (o, m, l) like ``naive_fwd``.
+    """
+    q3, lead = _as_slices(q)
+    k3, _ = _as_slices(k)
+    v3, _ = _as_slices(v)
+    G, n, d = q3.shape
+    nk = k3.shape[1]
+    if chunk is None:
+        chunk = max(1, int(math.ceil(math.sqrt(max(nk, 1)))))
+    scale = softmax_scale(d)
+    o = np.zeros((G, n, v3.shape[2]))
+    m_out = np.full((G, n), -np.inf)
+    l_out = np.zeros((G, n))
+    for g in range(G):
+        m = np.full(n, -np.inf)
+        l = np.zeros(n)
+        acc = np.zeros((n, v3.shape[2]))
+        for c0 in range(0, nk, chunk):
+            s = (q3[g] @ k3[g, c0:c0 + chunk].T) * scale
+            m_new = np.maximum(m, s.max(axis=1))
+            alpha = np.exp(m - m_new)
+            p = np.exp(s - m_new[:, None])
+            l = alpha * l + p.sum(axis=1)
+            acc = alpha[:, None] * acc + p @ v3[g, c0:c0 + chunk]
+            m = m_new
+        if nk > 0:
+            o[g] = acc / l[:, None]
+        m_out[g] = m
+        l_out[g] = l
+    return o.reshape(lead + o.shape[1:]), m_out.reshape(lead + (n,)), l_out.reshape(lead + (n,))
+
+
+def single_query(qv, k, v):
+    """One query, one key at a time, O(1) extra memory.
+
+    "Self-attention Does Not Need O(n^2) Memory" (abstract; 方法详解; English
+    digest method bullets): the score of each key is computed in turn and two
+    running quantities are updated, the weighted sum of values v* and the sum
+    of weights s*, both kept relative to the largest score m seen so far:
+        s     = q . k_i / sqrt(d)
+        m'    = max(m, s)
+        v*    = v* exp(m - m') + v_i exp(s - m')
+        s*    = s* exp(m - m') + exp(s - m')
+        m     = m'
+    The result v*/s* is formed once, after the last key. Pure Python over the
+    keys (numpy only for the length-d vectors); for small inputs.
+    qv: [d]; k, v: [n, d]. Returns (o [d], m, s*).
+    """
+    qv = np.asarray(qv, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    scale = softmax_scale(qv.shape[0])
+    m = -math.inf
+    vstar = np.zeros(v.shape[1])
+    sstar = 0.0
+    for i in range(k.shape[0]):
+        s = float(qv @ k[i]) * scale
+        m_new = max(m, s)
+        decay = math.exp(m - m_new) if m != -math.inf else 0.0
+        w = math.exp(s - m_new)
+        vstar = vstar * decay + v[i] * w
+        sstar = sstar * decay + w
+        m = m_new
+    return vstar / sstar, m, sstar
+
+
+def naive_bwd(q, k, v, do, rows=None, cols=None, row_block=1024):
+    """Gradients of the scalar L = sum(O * dO) with respect to Q, K and V.
+
+    The pages state only that the method stays differentiable and that the
+    backward pass recomputes chunk intermediates from a checkpoint instead of
+    storing them ("Self-attention Does Not Need O(n^2) Memory", abstract;
+    方法详解; English digest method bullets). They print no gradient formulas,
+    so this is the textbook Jacobian of O = softmax(S) V, S = QK^T / sqrt(d):
+        P      = softmax(S) (row-wise, as in ``naive_fwd``)
+        dV     = P^T dO
+        dP     = dO V^T
+        D_i    = sum_j P_ij dP_ij
+        dS     = P * (dP - D)           (elementwise; D broadcast over j)
+        dQ     = dS K / sqrt(d)
+        dK     = dS^T Q / sqrt(d)
+
+    Query rows are visited in blocks of ``row_block`` (each row's softmax is
+    complete within its block); dK and dV are sums over query rows and so are
+    accumulated block by block. ``rows`` restricts dQ to those query rows and
+    ``cols`` restricts dK, dV to those key rows (the full softmax is still
+    formed for every query row). Returns (dq, dk, dv).
+    """
+    q3, lead = _as_slices(q)
+    k3, _ = _as_slices(k)
+    v3, _ = _as_slices(v)
+    do3, _ = _as_slices(do)
+    G, n, d = q3.shape
+    nk = k3.shape[1]
+    ridx = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    cidx = np.arange(nk) if cols is None else np.asarray(cols, dtype=np.int64)
+    scale = softmax_scale(d)
+    dq = np.zeros((G, ridx.shape[0], d))
+    dk = np.zeros((G, cidx.shape[0], d))
+    dv = np.zeros((G, cidx.shape[0], v3.shape[2]))
+    if nk == 0 or n == 0:
+        return (dq.reshape(lead + dq.shape[1:]), dk.reshape(lead + dk.shape[1:]),
+                dv.reshape(lead + dv.shape[1:]))
+    # position of each requested query row in the dq output
+    want_row = np.full(n, -1, dtype=np.int64)
+    want_row[ridx] = np.arange(ridx.shape[0])
+    for g in range(G):
+        for b0 in range(0, n, row_block):
+            b1 = min(n, b0 + row_block)
+            s = (q3[g, b0:b1] @ k3[g].T) * scale
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            dp = do3[g, b0:b1] @ v3[g].T
+            D = (p * dp).sum(axis=1, keepdims=True)
+            ds = p * (dp - D)
+            wr = want_row[b0:b1]
+            hit = wr >= 0
+            if hit.any():
+                dq[g, wr[hit]] = (ds[hit] @ k3[g]) * scale
+            dk[g] += (ds[:, cidx].T @ q3[g, b0:b1]) * scale
+            dv[g] += p[:, cidx].T @ do3[g, b0:b1]
+    return (dq.reshape(lead + dq.shape[1:]), dk.reshape(lead + dk.shape[1:]),
+            dv.reshape(lead + dv.shape[1:]))
