@@ -1,0 +1,135 @@
+/*
+ * mea.h - C ABI of the memory-efficient exact attention library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What it computes. Exact softmax attention O = softmax(Q K^T / sqrt(d)) V
+ * ("Fast and memory-efficient exact attention 分析", section 数学表达形式;
+ * "当注意力成为瓶颈…", section 平方级的诅咒: the softmax normalises every row of
+ * the score matrix over all keys), and its gradient. As in "Self-attention
+ * Does Not Need O(n^2) Memory" (abstract; method sections), keys and values
+ * are visited in tiles while every query row keeps a running maximum and a
+ * running sum of exponentiated scores, and the division by that sum happens
+ * once at the end, so no n x n matrix is ever stored. The backward pass
+ * recomputes score tiles from the per-row statistics the forward pass saved
+ * (the pages' checkpoint-and-recompute differentiation).
+ *
+ * Conventions shared by every entry point.
+ *  - Tensors q, k, v, o, dO, dq, dk, dv are contiguous row-major
+ *    [B, H, n, d] arrays in the element type `dt` (d fastest). Self-attention:
+ *    queries and keys have the same length n. No mask, no causal structure,
+ *    no dropout. The score scale is fixed at 1/sqrt(d).
+ *  - Every pointer is a DEVICE pointer on the current HIP device, owned by the
+ *    caller, and must be 16-byte aligned. The library allocates no device
+ *    memory and keeps no state between calls; it is thread-safe.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *    the null stream). Nothing is synchronised. Inputs must stay valid and
+ *    outputs untouched until the stream reaches the work.
+ *  - Arguments are validated on the host before any HIP call, in this order:
+ *    dtype, shape, head dimension, null pointers, alignment, workspace. A
+ *    call with B, H or n equal to 0 does nothing and returns MEA_OK (pointers
+ *    may then be NULL). MEA_ERR_LAUNCH reports a launch failure seen by
+ *    hipGetLastError right after the launch; faults during execution surface
+ *    at the caller's next synchronisation, as with any HIP kernel.
+ *  - Supported: dt in {MEA_DTYPE_BF16, MEA_DTYPE_F32}, d in {64, 128},
+ *    1 <= n <= 2^24, B*H <= 2^24.
+ *  - Accuracy: bf16 inputs are multiplied exactly on bf16 MFMA with fp32
+ *    accumulation; probabilities are rounded to bf16 (round-to-nearest-even)
+ *    for the P V product; outputs are rounded to bf16 (RNE). fp32 inputs
+ *    form scores on fp64 MFMA (exact products, fp64 sums), subtract the row
+ *    maximum in fp64, then exponentiate and accumulate P V in fp32.
+ */
+#ifndef MEA_H
+#define MEA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MEA_DTYPE_F32 = 0,  /* IEEE binary32 */
+  MEA_DTYPE_BF16 = 1  /* bfloat16 */
+} mea_dtype_t;
+
+typedef enum {
+  MEA_OK = 0,
+  MEA_ERR_NULL = 1,        /* a required pointer is NULL */
+  MEA_ERR_SHAPE = 2,       /* negative or too large B, H, n */
+  MEA_ERR_UNSUPPORTED = 3, /* unsupported dtype or head dimension d */
+  MEA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  MEA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+  MEA_ERR_LAUNCH = 6       /* the HIP runtime rejected a kernel launch */
+} mea_status_t;
+
+/*
+ * attn_fwd - forward pass.
+ *
+ * o[b,h,i,:] = sum_j softmax_j(q[b,h,i,:] . k[b,h,j,:] / sqrt(d)) v[b,h,j,:]
+ *
+ * Keys and values are swept tile by tile with a running maximum and running
+ * sum per query row, normalising once at the end ("Self-attention Does Not
+ * Need O(n^2) Memory": abstract; method bullets of the English digest;
+ * "当注意力成为瓶颈…", section IO感知, two-block merge).
+ *
+ * q, k, v : inputs [B,H,n,d] in dt.            o : output [B,H,n,d] in dt.
+ * row_max : output fp32 [B,H,n] or NULL: m_i = max_j q_i.k_j / sqrt(d)
+ *           (natural units of the scaled score).
+ * row_sum : output fp32 [B,H,n] or NULL: l_i = sum_j exp(q_i.k_j/sqrt(d) - m_i).
+ *           The two statistics are what attn_bwd needs; pass both or neither
+ *           (passing exactly one is MEA_ERR_NULL).
+ * No workspace: the only memory beyond inputs and outputs is the optional
+ * 8*B*H*n bytes of statistics.
+ */
+mea_status_t attn_fwd(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d,
+                      const void* q, const void* k, const void* v, void* o,
+                      float* row_max, float* row_sum, void* stream);
+
+/*
+ * attn_bwd_workspace_bytes - bytes of device workspace attn_bwd needs:
+ * 8*B*H*n (two fp32 values per query row: D_i = sum_c dO_ic * O_ic and the
+ * base-2 log-sum-exp of the row). Returns 0 for empty or invalid shapes.
+ */
+size_t attn_bwd_workspace_bytes(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d);
+
+/*
+ * attn_bwd - backward pass of L = sum(O * dO), by recomputation.
+ *
+ * The pages give no gradient formulas, only that differentiation recomputes
+ * chunk intermediates instead of storing them ("Self-attention Does Not Need
+ * O(n^2) Memory": abstract; 方法详解; English digest method bullets). The
+ * textbook Jacobian of the softmax is used:
+ *   P = softmax(S), S = Q K^T / sqrt(d);  dV = P^T dO;  dP = dO V^T;
+ *   D_i = sum_c dO_ic O_ic;  dS = P * (dP - D);  dQ = dS K / sqrt(d);
+ *   dK = dS^T Q / sqrt(d).
+ * P is rebuilt tile by tile from row_max and row_sum; no n x n array exists.
+ *
+ * q, k, v, o, dO : inputs [B,H,n,d] in dt (o from attn_fwd on the same q,k,v).
+ * row_max, row_sum : the fp32 [B,H,n] statistics attn_fwd wrote for these
+ *                    inputs (required).
+ * dq, dk, dv : outputs [B,H,n,d] in dt; fully overwritten.
+ * workspace  : device scratch of at least attn_bwd_workspace_bytes(...) bytes,
+ *              16-byte aligned, owned by the caller; its contents on entry do
+ *              not matter and on return are unspecified.
+ * Supported: dt = MEA_DTYPE_BF16 with d in {64, 128}. Other combinations
+ * return MEA_ERR_UNSUPPORTED.
+ */
+mea_status_t attn_bwd(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d,
+                      const void* q, const void* k, const void* v, const void* o,
+                      const void* dO, const float* row_max, const float* row_sum,
+                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* attn_status_str - static, NUL-terminated name of a status code
+ * ("MEA_OK", "MEA_ERR_NULL", ...); "MEA_UNKNOWN_STATUS" for other values. */
+const char* attn_status_str(mea_status_t s);
+
+/* mea_version - library version as 10000*major + 100*minor + patch. */
+int mea_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MEA_H */

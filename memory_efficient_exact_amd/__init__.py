@@ -1,0 +1,194 @@
+"""Memory-efficient exact attention on AMD MI355X (gfx950).
+
+Thin ctypes binding over ``libmea.so`` (C ABI in ``include/mea.h``). The
+functions here only marshal arguments: they check tensor placement and
+layout, allocate outputs with torch when the caller does not pass them, and
+call the C entry points of the same names on the current torch stream. All
+arithmetic runs in the library's HIP kernels; there is no fallback path, and
+every function raises if the library has not been built.
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "MeaError", "DTYPE_F32", "DTYPE_BF16", "lib", "library_path",
+    "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str", "mea_version",
+]
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+_STATUS = ["MEA_OK", "MEA_ERR_NULL", "MEA_ERR_SHAPE", "MEA_ERR_UNSUPPORTED",
+           "MEA_ERR_ALIGN", "MEA_ERR_WORKSPACE", "MEA_ERR_LAUNCH"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def library_path():
+    return os.path.join(_HERE, "libmea.so")
+
+
+class MeaError(RuntimeError):
+    """A non-OK status returned by the library."""
+
+    def __init__(self, fn, status):
+        self.status = int(status)
+        super().__init__(f"{fn} failed: {attn_status_str(self.status)} ({self.status})")
+
+
+def lib():
+    """The loaded ``libmea.so`` (ctypes.CDLL), with argument types declared."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m memory_efficient_exact_amd.build` "
+            "(or __graft_entry__.build()). There is no fallback implementation.")
+    L = ctypes.CDLL(path)
+    i64, vp, i32, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.attn_fwd.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+    L.attn_fwd.restype = i32
+    L.attn_bwd_workspace_bytes.argtypes = [i32, i64, i64, i64, i64]
+    L.attn_bwd_workspace_bytes.restype = sz
+    L.attn_bwd.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.attn_bwd.restype = i32
+    L.attn_status_str.argtypes = [i32]
+    L.attn_status_str.restype = ctypes.c_char_p
+    L.mea_version.argtypes = []
+    L.mea_version.restype = i32
+    _LIB = L
+    return L
+
+
+def attn_status_str(status):
+    """Name of a status code, from the library (falls back to the table if unbuilt)."""
+    try:
+        return lib().attn_status_str(int(status)).decode()
+    except RuntimeError:
+        s = int(status)
+        return _STATUS[s] if 0 <= s < len(_STATUS) else "MEA_UNKNOWN_STATUS"
+
+
+def mea_version():
+    return lib().mea_version()
+
+
+def attn_bwd_workspace_bytes(dt, B, H, n, d):
+    return lib().attn_bwd_workspace_bytes(int(dt), int(B), int(H), int(n), int(d))
+
+
+# ------------------------------------------------------------ torch marshalling
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise ValueError(f"unsupported dtype {t.dtype}; expected torch.bfloat16 or torch.float32")
+
+
+def _check(name, t, like):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.device != like.device:
+        raise ValueError(f"{name} is on {t.device}, expected {like.device}")
+    if tuple(t.shape) != tuple(like.shape) or t.dtype != like.dtype:
+        raise ValueError(f"{name} must match q: shape {tuple(like.shape)} dtype {like.dtype}, "
+                         f"got {tuple(t.shape)} {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_stat(name, t, q):
+    if not t.is_cuda or t.device != q.device:
+        raise ValueError(f"{name} must be on {q.device}")
+    if tuple(t.shape) != tuple(q.shape[:3]):
+        raise ValueError(f"{name} must have shape {tuple(q.shape[:3])}, got {tuple(t.shape)}")
+    import torch
+    if t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous float32")
+
+
+def _stream(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def attn_fwd(q, k, v, out=None, row_max=None, row_sum=None, stats=True, stream=None):
+    """O = softmax(q k^T / sqrt(d)) v for contiguous [B, H, n, d] GPU tensors.
+
+    Returns (o, row_max, row_sum); the statistics are None when ``stats`` is
+    False and none are passed. Outputs not passed are allocated with torch.
+    Enqueued on ``stream`` (default: torch's current stream); not synchronised.
+    """
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, n, d]")
+    dt = _dtype_code(q)
+    _check("q", q, q)
+    _check("k", k, q)
+    _check("v", v, q)
+    if out is None:
+        out = torch.empty_like(q)
+    _check("out", out, q)
+    if (row_max is None) != (row_sum is None):
+        raise ValueError("pass both row_max and row_sum, or neither")
+    if row_max is None and stats:
+        row_max = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+        row_sum = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if row_max is not None:
+        _check_stat("row_max", row_max, q)
+        _check_stat("row_sum", row_sum, q)
+    B, H, n, d = q.shape
+    with torch.cuda.device(q.device):
+        st = lib().attn_fwd(dt, B, H, n, d, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                            _ptr(row_max), _ptr(row_sum), _stream(stream, q.device))
+    if st != 0:
+        raise MeaError("attn_fwd", st)
+    return out, row_max, row_sum
+
+
+def attn_bwd(q, k, v, o, do, row_max, row_sum, dq=None, dk=None, dv=None, workspace=None,
+             stream=None):
+    """Gradients (dq, dk, dv) of sum(o * do), recomputing P from the saved
+    row statistics. Same tensor conventions as ``attn_fwd``; ``workspace`` is
+    a GPU tensor of at least ``attn_bwd_workspace_bytes`` bytes (allocated if
+    not passed)."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, n, d]")
+    dt = _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(name, t, q)
+    _check_stat("row_max", row_max, q)
+    _check_stat("row_sum", row_sum, q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(name, t, q)
+    B, H, n, d = q.shape
+    need = attn_bwd_workspace_bytes(dt, B, H, n, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    wbytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        st = lib().attn_bwd(dt, B, H, n, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+                            _ptr(row_max), _ptr(row_sum), _ptr(dq), _ptr(dk), _ptr(dv),
+                            _ptr(workspace), wbytes, _stream(stream, q.device))
+    if st != 0:
+        raise MeaError("attn_bwd", st)
+    return dq, dk, dv

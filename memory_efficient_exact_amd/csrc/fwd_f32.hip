@@ -1,0 +1,212 @@
+// Forward attention for fp32 inputs on gfx950, with scores formed in fp64.
+//
+// Same method as the bf16 kernel ("Self-attention Does Not Need O(n^2)
+// Memory": running maximum and running sums per query, one division at the
+// end; "当注意力成为瓶颈…", section IO感知: per-tile merge). Precision: an
+// fp32 product is exact in fp64, so S^T = K Q^T runs on fp64 MFMA
+// (16x16x4) and the row maximum is subtracted in fp64. Only the difference
+// s - m (<= 0) is rounded to fp32 before the base-2 exponential; the weights,
+// their sum and P V (fp32 MFMA 16x16x4) are fp32. With scores of magnitude
+// ~1e4 an fp32 score would carry an absolute error near 1e-3, enough to move
+// the weights of near-tied keys by far more than the 1e-5 output tolerance.
+//
+// Work split: 4 waves, 16 query rows per wave; K/V tiles of 32 keys in LDS,
+// double-buffered, rows padded so the column reads of both MFMA operands hit
+// distinct banks. The score tile is transposed (lane = query), so the per-row
+// state lives in registers; four lanes (l, l^16, l^32, l^48) share a query.
+#include "mea_device.h"
+#include "mea_launch.h"
+
+namespace mea {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBQ = 16 * kWaves;  // query rows per workgroup
+constexpr int kBC = 32;           // keys per tile
+
+__device__ __forceinline__ float xor16f(float x) { return __shfl_xor(x, 16, 64); }
+__device__ __forceinline__ double xor16d(double x) { return __shfl_xor(x, 16, 64); }
+__device__ __forceinline__ double xor32d(double x) { return __shfl_xor(x, 32, 64); }
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ Mx, float* __restrict__ Ls,
+    int n, int qtiles, int total, double C64, double scale64) {
+  constexpr int KS = D + 4;   // K row stride (floats): 16-byte pad
+  constexpr int VS = D + 16;  // V row stride (floats): 64-byte pad
+  constexpr int KK = D / 4;   // k-steps of the fp64 score MFMA
+  constexpr int DB = D / 16;  // 16-wide output column blocks
+  constexpr int KB = kBC / 16;
+  constexpr int kCPR = D / 4;  // 16-byte chunks per row
+  constexpr int kLoads = kBC * D / 4 / kThreads;
+  static_assert(kLoads * 4 * kThreads == kBC * D, "tile split");
+
+  __shared__ __attribute__((aligned(16))) float sK[2][kBC * KS];
+  __shared__ __attribute__((aligned(16))) float sV[2][kBC * VS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int g4 = lane >> 4;
+
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int bh = tile / qtiles;
+  const int qt = tile - bh * qtiles;
+  const int64_t base = (int64_t)bh * n * D;
+  const float* Kh = K + base;
+  const float* Vh = V + base;
+  const int row = qt * kBQ + wave * 16 + l16;  // this lane's query row
+
+  // B operand of S^T = K Q^T: Q[row][4*kk + g4] as fp64
+  double qd[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    qd[kk] = row < n ? (double)Q[base + (int64_t)row * D + 4 * kk + g4] : 0.0;
+
+  double m_run = -INFINITY;  // running max of raw scores (fp64)
+  float l_run = 0.f;         // this lane's share of the running sum
+  f32x4 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x4{};
+
+  u32x4 kreg[kLoads], vreg[kLoads];
+  auto gload = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int c = tid + i * kThreads;
+      const int r = c / kCPR;
+      const int ch = c - r * kCPR;
+      if (j0 + r < n) {
+        const int64_t off = (int64_t)(j0 + r) * D + ch * 4;
+        kreg[i] = *reinterpret_cast<const u32x4*>(Kh + off);
+        vreg[i] = *reinterpret_cast<const u32x4*>(Vh + off);
+      } else {
+        kreg[i] = u32x4{};
+        vreg[i] = u32x4{};
+      }
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int c = tid + i * kThreads;
+      const int r = c / kCPR;
+      const int ch = c - r * kCPR;
+      *reinterpret_cast<u32x4*>(&sK[buf][r * KS + ch * 4]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&sV[buf][r * VS + ch * 4]) = vreg[i];
+    }
+  };
+
+  const int ntiles = (n + kBC - 1) / kBC;
+  gload(0);
+  swrite(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const int j0 = t * kBC;
+    if (t + 1 < ntiles) gload(j0 + kBC);
+    const float* ks = sK[buf];
+    const float* vs = sV[buf];
+
+    // S^T block kb: lane holds query l16 and, in register r, key 16*kb + 4*r + g4
+    f64x4 s[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = f64x4{};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const double a = (double)ks[(kb * 16 + l16) * KS + 4 * kk + g4];
+        s[kb] = mfma_f64_16x16x4(a, qd[kk], s[kb]);
+      }
+    }
+    if (j0 + kBC > n) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (j0 + kb * 16 + 4 * r + g4 >= n) s[kb][r] = -INFINITY;
+    }
+
+    double mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmax(mx, s[kb][r]);
+    mx = fmax(mx, xor16d(mx));
+    mx = fmax(mx, xor32d(mx));
+    const double m_new = fmax(m_run, mx);
+    const float alpha = fast_exp2((float)((m_run - m_new) * C64));
+    float p[KB][4];
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[kb][r] = fast_exp2((float)((s[kb][r] - m_new) * C64));
+        ls += p[kb][r];
+      }
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+
+    // O^T += V^T P^T: k-step (kb, c) covers keys 16*kb + 4*c + 0..3;
+    // B = P^T[key 16*kb + 4*c + g4][query l16] is register c of block kb
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float* vrow = vs + (kb * 16 + 4 * c + g4) * VS + l16;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] = mfma_f32_16x16x4(vrow[db * 16], p[kb][c], acc[db]);
+      }
+
+    if (t + 1 < ntiles) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  // lanes l, l^16, l^32, l^48 share query l16: combine their partial sums
+  float l_tot = l_run + xor16f(l_run);
+  l_tot = l_tot + xor32(l_tot);
+  const float inv = 1.f / l_tot;
+  if (row < n) {
+    // acc[db] register r holds O[row][16*db + 4*g4 + r]
+    float* orow = O + base + (int64_t)row * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      f32x4 w = acc[db] * inv;
+      *reinterpret_cast<f32x4*>(orow + db * 16 + 4 * g4) = w;
+    }
+    if (Mx != nullptr && g4 == 0) {
+      Mx[(int64_t)bh * n + row] = (float)(m_run * scale64);
+      Ls[(int64_t)bh * n + row] = l_tot;
+    }
+  }
+}
+
+template <int D>
+hipError_t launch(int64_t BH, int n, const void* q, const void* k, const void* v, void* o,
+                  float* m, float* l, hipStream_t stream) {
+  const int qtiles = (n + kBQ - 1) / kBQ;
+  const int64_t total = BH * qtiles;
+  const double scale64 = 1.0 / sqrt((double)D);
+  const double C64 = 1.4426950408889634 * scale64;
+  hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)total), dim3(kThreads), 0, stream,
+                     (const float*)q, (const float*)k, (const float*)v, (float*)o, m, l, n, qtiles,
+                     (int)total, C64, scale64);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32(int d, int64_t BH, int n, const void* q, const void* k, const void* v,
+                          void* o, float* m, float* l, hipStream_t stream) {
+  if (d == 64) return launch<64>(BH, n, q, k, v, o, m, l, stream);
+  return launch<128>(BH, n, q, k, v, o, m, l, stream);
+}
+
+}  // namespace mea

@@ -1,0 +1,104 @@
+// Device-side building blocks for the gfx950 attention kernels: vector types,
+// MFMA wrappers with their lane layouts, the LDS tile swizzle, transposed LDS
+// reads and wave-level helpers. Host code never includes this file.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mea {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define MEA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- MFMA
+// v_mfma_f32_32x32x16_bf16, D[32x32] += A[32x16] B[16x32], wave64.
+//   A: lane l holds A[i = l%32][k = 8*(l/32) + e], e = 0..7
+//   B: lane l holds B[k = 8*(l/32) + e][j = l%32]
+//   D: lane l, register r holds D[i = 8*(r/4) + 4*(l/32) + r%4][j = l%32]
+// (layouts checked on gfx950 hardware with exact small-integer products).
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f64_16x16x4_f64, D[16x16] += A[16x4] B[4x16].
+//   A: lane l holds A[i = l%16][k = l/16];  B: lane l holds B[k = l/16][j = l%16]
+//   D: lane l, register r holds D[i = 4*r + l/16][j = l%16]
+__device__ __forceinline__ f64x4 mfma_f64_16x16x4(double a, double b, f64x4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x4_f32, D[16x16] += A[16x4] B[4x16].
+//   A: lane l holds A[i = l%16][k = l/16];  B: lane l holds B[k = l/16][j = l%16]
+//   D: lane l, register r holds D[i = 4*(l/16) + r][j = l%16]
+__device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- LDS tiles
+// A bf16 tile of R rows x D columns is stored row-major in LDS, one row after
+// another, with its 16-byte chunks permuted inside each row by XOR with a
+// row-dependent key. The permutation keeps 8-byte halves together, so both
+// 16-byte row reads and 8-byte transposed reads see whole pieces. Keys spread
+// 16 consecutive rows at the same logical chunk over all 64 banks.
+template <int D>
+__device__ __forceinline__ int swz_chunk(int row, int chunk) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  return D == 64 ? (chunk ^ ((row >> 1) & 7)) : (chunk ^ (row & 15));
+}
+
+// element offset of (row, col) in a swizzled bf16 tile; col must be a multiple of 4
+template <int D>
+__device__ __forceinline__ int swz_off(int row, int col) {
+  return row * D + swz_chunk<D>(row, col >> 3) * 8 + (col & 7);
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// ds_read_b64_tr_b16: each lane supplies the address of 4 consecutive b16
+// values (8 bytes). Within every group of 16 lanes, output lane i, element e
+// is element i%4 of the 8 bytes addressed by lane 4*e + i/4 of its group.
+// If lane j of a group addresses row (base + j/4), columns c0 + 4*(j%4)..+3
+// of a row-major tile, output lane i holds rows base..base+3 of column c0 + i.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const bf16* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (MEA_LDS i16x4*)((MEA_LDS char*)((uintptr_t)p)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// ---------------------------------------------------------------- wave helpers
+// value from lane l ^ 32
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Global->LDS/row-major block index remap. The hardware hands consecutive
+// workgroup ids to the 8 XCDs in turn; remapping makes the ids that run on
+// one XCD consecutive in the logical order, so the query tiles of one head
+// (which stream the same K and V) share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  constexpr int kXcd = 8;
+  const int per = total / kXcd;  // whole rounds
+  const int full = per * kXcd;
+  if (bid >= full) return bid;   // ragged tail keeps its order
+  return (bid % kXcd) * per + bid / kXcd;
+}
+
+}  // namespace mea
