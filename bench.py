@@ -1,0 +1,186 @@
+"""Benchmark: exact attention forward + recompute backward on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+attn_fwd (O and the per-row statistics) followed by attn_bwd (dQ, dK, dV),
+both through the C ABI, on the n = 16384 bf16 workload
+(B=1, H=16, n=16384, d=64; Q, K, V, dO ~ N(0,1) from a fixed seed).
+
+FLOP convention (algorithmic): forward 4*B*H*n^2*d (QK^T and PV), backward
+10*B*H*n^2*d (score recompute, dV, dP, dQ, dK). ``value`` = 14*B*H*n^2*d per
+step / step time, in TFLOP/s. Inputs are resident in HBM before timing.
+
+Prints exactly one JSON line on stdout (everything else goes to stderr).
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOP/s at n=16384 bf16 on 1 MI355X; % MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w):
+    """The fp64 oracle as it stands, on one of the workload's heads (all n
+    query rows, forward then backward), timed on this host's cores."""
+    import numpy as np
+
+    import inputgen
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = os.cpu_count() or 1
+    t = inputgen.draw(1, 1, w.n, w.d, w.dtype, seed=w.seed, with_do=True)
+    q, k, v, do = (inputgen.to_f64(t[x]) for x in ("q", "k", "v", "do"))
+    t0 = time.perf_counter()
+    oracle.naive_fwd(q, k, v)
+    t1 = time.perf_counter()
+    oracle.naive_bwd(q, k, v, do)
+    t2 = time.perf_counter()
+    flops = 14.0 * w.n * w.n * w.d
+    return {
+        "value": flops / (t2 - t0) / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"one head (B=1, H=1, n={w.n}, d={w.d}) of the workload, fp64 oracle "
+                   f"naive_fwd + naive_bwd over all rows; fwd {t1 - t0:.2f} s, bwd {t2 - t1:.2f} s"),
+        "host": {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+                 "machine": platform.processor() or platform.machine()},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the attention "
+              "kernels shard by (batch, head) with no communication, so per-GPU throughput "
+              "is the single-GPU number", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import inputgen
+    import memory_efficient_exact_amd as mea
+
+    w = inputgen.WORKLOADS["c3_long_bf16"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = inputgen.draw(w.B, w.H, w.n, w.d, w.dtype, seed=w.seed, with_do=True)
+    q, k, v, do = (t[x].to(dev) for x in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    m = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    l = torch.empty_like(m)
+    ws = torch.empty(mea.attn_bwd_workspace_bytes(mea.DTYPE_BF16, w.B, w.H, w.n, w.d),
+                     dtype=torch.uint8, device=dev)
+    io_bytes = sum(x.numel() * x.element_size() for x in (q, k, v, do, o, dq, dk, dv, m, l))
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mea.attn_fwd(q, k, v, out=o, row_max=m, row_sum=l, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        mea.attn_bwd(q, k, v, o, do, m, l, dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    before = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize(dev)
+    peak_extra = torch.cuda.max_memory_allocated(dev) - before
+    total_ms = start.elapsed_time(stop)
+    ms = total_ms / args.steps
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    fwd_flops, bwd_flops = w.fwd_flops(), w.bwd_flops()
+    value = (fwd_flops + bwd_flops) / (ms * 1e-3) / 1e12
+    f_avg = statistics.mean(fwd_ms)
+    b_avg = statistics.mean(bwd_ms)
+    fwd_tf = fwd_flops / (f_avg * 1e-3) / 1e12
+    bwd_tf = bwd_flops / (b_avg * 1e-3) / 1e12
+    log(f"step {ms:.3f} ms | fwd {f_avg:.3f} ms ({fwd_tf:.1f} TFLOP/s, "
+        f"{100 * fwd_tf / PEAK_BF16_TFLOPS:.1f}% of peak) | bwd {b_avg:.3f} ms ({bwd_tf:.1f} TFLOP/s)")
+
+    # Roofline of the forward kernel (one launch per attn_fwd call, timed by the
+    # events around that call on the launch stream).
+    roofline = {
+        "kernel": "fwd_bf16_kernel<64,2>",
+        "bound": "mfma",
+        "achieved": fwd_tf,
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": fwd_tf / PEAK_BF16_TFLOPS,
+        "traffic": None,
+        "avg_launch_ms": f_avg,
+        "flops_per_launch": fwd_flops,
+    }
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "self-attention n=16384 bf16, forward + recompute backward",
+                   "B": w.B, "H": w.H, "n": w.n, "d": w.d, "seed": w.seed,
+                   "parallelism": "single GPU"},
+        "fwd": {"ms": f_avg, "ms_min": min(fwd_ms), "tflops": fwd_tf,
+                "pct_peak": 100 * fwd_tf / PEAK_BF16_TFLOPS},
+        "bwd": {"ms": b_avg, "ms_min": min(bwd_ms), "tflops": bwd_tf,
+                "pct_peak": 100 * bwd_tf / PEAK_BF16_TFLOPS},
+        "pct_peak": 100 * value / PEAK_BF16_TFLOPS,
+        "memory": {"io_bytes": io_bytes, "peak_extra_bytes_during_steps": peak_extra,
+                   "library_overhead_bytes": 8 * w.B * w.H * w.n + ws.numel(),
+                   "n2_fp32_score_matrix_bytes": 4 * w.B * w.H * w.n * w.n},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on one head ...")
+        out["cpu_baseline"] = cpu_baseline(w)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,6 +21,10 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # no packed fp32 VALU instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no implicit mul+add fusion: the kernels write every FMA they want
+    # explicitly, and the softmax bookkeeping relies on rounded products
+    # (fl(m*C)) staying rounded
+    "-ffp-contract=off",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

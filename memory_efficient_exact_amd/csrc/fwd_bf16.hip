@@ -78,12 +78,17 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
     }
   }
 
-  float m_run[QB];  // running max of raw scores q.k
-  float l_run[QB];  // this lane's share of the running sum
+  // Per query row: the running max m of the raw scores q.k, its rounded
+  // product mC = fl(m * C) (every weight is formed as exp2(fl(x*C - mC)) with
+  // one FMA), and this lane's share of the running sum of those weights.
+  float m_run[QB];
+  float mC_run[QB];
+  float l_run[QB];
   f32x16 acc[QB][DB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_run[qb] = -INFINITY;
+    mC_run[qb] = -INFINITY;
     l_run[qb] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
@@ -175,8 +180,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
       mx = fmaxf(mx, xor32(mx));
       const float m_new = fmaxf(m_run[qb], mx);
-      const float alpha = fast_exp2((m_run[qb] - m_new) * C);
       const float mC = m_new * C;
+      // rescale by the ratio of the rounded references, so that all weights in
+      // l and acc stay relative to the same mC
+      const float alpha = fast_exp2(mC_run[qb] - mC);
       float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -188,6 +195,7 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
         }
       l_run[qb] = l_run[qb] * alpha + ls;
       m_run[qb] = m_new;
+      mC_run[qb] = mC;
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
     }
@@ -228,8 +236,12 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
           *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * r4 + 4 * hi) = w;
         }
       if (Mx != nullptr && hi == 0) {
+        // The weights summed in l_tot are 2^eps times exp(s - m), where
+        // eps = m*C - fl(m*C) is the rounding residual of the reference
+        // (exact through one FMA); report l for the exact maximum.
+        const float eps = __builtin_fmaf(m_run[qb], C, -mC_run[qb]);
         Mx[(int64_t)bh * n + row] = m_run[qb] * scale;
-        Ls[(int64_t)bh * n + row] = l_tot;
+        Ls[(int64_t)bh * n + row] = l_tot * fast_exp2(-eps);
       }
     }
   }
