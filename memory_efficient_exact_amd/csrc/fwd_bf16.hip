@@ -5,21 +5,34 @@
 // Method: "Self-attention Does Not Need O(n^2) Memory" (abstract; method
 // sections of both digests): postpone the softmax division to the end, keep
 // a weighted value sum and a weight sum per query, track the maximum score
-// for stability, and visit keys/values in chunks. The per-tile update is the
-// two-block merge of "当注意力成为瓶颈…", section IO感知, applied once per tile.
+// for stability, and visit keys/values in chunks. The per-block update is the
+// two-block merge of "当注意力成为瓶颈…", section IO感知, applied once per
+// 32-key block.
 //
-// Layout of the work (per workgroup of 4 waves):
+// Layout of the work (per workgroup of 4 waves, two workgroups per CU):
 //  * each wave owns QB blocks of 32 query rows; the workgroup owns 4*QB*32;
-//  * K and V tiles of 64 keys are staged in LDS, double-buffered, with the
+//  * K and V tiles of BC keys are copied straight from HBM into LDS
+//    (global_load_lds, no register staging), double-buffered, with the
 //    16-byte chunks of each row swizzled (see mea_device.h);
 //  * scores are formed transposed, S^T = K Q^T, on 32x32x16 bf16 MFMA, so
 //    that each lane holds one query's scores for 16 keys per 32-key block:
-//    the row maximum is a register reduction plus one exchange with lane
-//    l^32, and the per-row rescale factor is a per-lane scalar;
+//    the row maximum is a register reduction plus one v_permlane32_swap, and
+//    every per-row factor is a per-lane scalar;
 //  * the output is accumulated transposed, O^T += V^T P^T: P^T comes straight
 //    from the S^T accumulators (rounded to bf16), V^T from transposed LDS
-//    reads of the row-major V tile;
+//    reads (ds_read_b64_tr_b16) of the row-major V tile;
 //  * exponentials are base 2 with log2(e)/sqrt(d) folded into one FMA.
+//
+// Reference maximum. Weights are formed as p = exp2(x*C - R) with a per-row
+// reference R that is refreshed to fl(m*C) (m = running max of the raw
+// scores x = q.k) only when some row's maximum has grown past R + 8, at
+// which point acc and l are multiplied by exp2(R_old - R_new). So p <= 2^8
+// (no overflow, same bf16 relative precision), the output acc/l is exact as
+// before, and the O(d) rescale of the accumulators is skipped for almost every
+// block. The true running max m is tracked separately; the statistics are
+// reported for it: l = sum_j exp(s_j - m) = l_R * exp2(R - m*C).
+#include <type_traits>
+
 #include "mea_device.h"
 #include "mea_launch.h"
 
@@ -28,25 +41,26 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBC = 64;  // keys per tile
+constexpr float kRefSlack = 8.0f;  // log2 units a row max may exceed its reference
 
-template <int D, int QB>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
+template <int D, int QB, int BC>
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ Mx, float* __restrict__ Ls,
     int n, int qtiles, int total, float C, float scale) {
-  constexpr int kBQ = kWaves * QB * 32;   // query rows per workgroup
-  constexpr int DK = D / 16;              // k-steps of the score MFMA
-  constexpr int DB = D / 32;              // 32-wide output column blocks
-  constexpr int KB = kBC / 32;            // 32-key blocks per tile
-  constexpr int NC = kBC / 16;            // 16-key chunks per tile (PV k-steps)
-  constexpr int kTile = kBC * D;          // elements per K or V tile
-  constexpr int kCPR = D / 8;             // 16-byte chunks per row
-  constexpr int kLoads = kTile / 8 / kThreads;
-  static_assert(kLoads * 8 * kThreads == kTile, "tile split");
+  constexpr int kBQ = kWaves * QB * 32;  // query rows per workgroup
+  constexpr int DK = D / 16;             // k-steps of the score MFMA
+  constexpr int DB = D / 32;             // 32-wide output column blocks
+  constexpr int SB = BC / 32;            // 32-key blocks per LDS tile
+  constexpr int kTile = BC * D;          // elements per K or V tile
+  constexpr int kBlocks = kTile / 512;   // 1 KiB DMA blocks per tile
+  constexpr int kBPW = kBlocks / kWaves; // DMA blocks per wave per tile
+  constexpr int RPB = 512 / D;           // rows per DMA block
+  constexpr int LPR = D / 8;             // lanes per row in a DMA block
+  static_assert(kBPW * kWaves == kBlocks, "tile split");
 
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][kTile];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][kTile];
+  __shared__ __attribute__((aligned(1024))) bf16 sK[2][kTile];
+  __shared__ __attribute__((aligned(1024))) bf16 sV[2][kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -70,63 +84,40 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
     const int row = q0 + qb * 32 + l32;
 #pragma unroll
     for (int dk = 0; dk < DK; ++dk) {
-      if (row < n) {
-        qf[qb][dk] = *reinterpret_cast<const bf16x8*>(Qh + (int64_t)row * D + dk * 16 + 8 * hi);
-      } else {
-        qf[qb][dk] = bf16x8{};
-      }
+      qf[qb][dk] = row < n ? *reinterpret_cast<const bf16x8*>(Qh + (int64_t)row * D + dk * 16 + 8 * hi)
+                           : bf16x8{};
     }
   }
 
-  // Per query row: the running max m of the raw scores q.k, its rounded
-  // product mC = fl(m * C) (every weight is formed as exp2(fl(x*C - mC)) with
-  // one FMA), and this lane's share of the running sum of those weights.
-  float m_run[QB];
-  float mC_run[QB];
-  float l_run[QB];
+  float m_run[QB];  // running max of raw scores q.k (exact)
+  float ref[QB];    // reference R (see header)
+  float l_run[QB];  // this lane's share of sum_j exp2(x_j*C - R)
   f32x16 acc[QB][DB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_run[qb] = -INFINITY;
-    mC_run[qb] = -INFINITY;
+    ref[qb] = -INFINITY;
     l_run[qb] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
   }
 
-  u32x4 kreg[kLoads], vreg[kLoads];
-  auto gload = [&](int j0) {
+  // DMA of the K and V tile starting at key j0 into buffer `buf`. Block b of
+  // the tile holds rows b*RPB.. ; lane l fills physical chunk l%LPR of row
+  // b*RPB + l/LPR, so it fetches the logical chunk that the swizzle puts
+  // there. Rows past n repeat row n-1 (their scores are masked to -inf).
+  auto issue = [&](int buf, int j0) {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c / kCPR;
-      const int ch = c - r * kCPR;
-      if (j0 + r < n) {
-        const int64_t off = (int64_t)(j0 + r) * D + ch * 8;
-        kreg[i] = *reinterpret_cast<const u32x4*>(Kh + off);
-        vreg[i] = *reinterpret_cast<const u32x4*>(Vh + off);
-      } else {
-        kreg[i] = u32x4{};
-        vreg[i] = u32x4{};
-      }
+    for (int i = 0; i < kBPW; ++i) {
+      const int b = wave * kBPW + i;
+      const int r = b * RPB + lane / LPR;
+      const int ch = swz_chunk<D>(r, lane % LPR);
+      const int src = min(j0 + r, n - 1);
+      const int64_t off = (int64_t)src * D + ch * 8;
+      dma16(Kh + off, &sK[buf][b * 512]);
+      dma16(Vh + off, &sV[buf][b * 512]);
     }
   };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c / kCPR;
-      const int ch = c - r * kCPR;
-      const int off = r * D + swz_chunk<D>(r, ch) * 8;
-      *reinterpret_cast<u32x4*>(&sK[buf][off]) = kreg[i];
-      *reinterpret_cast<u32x4*>(&sV[buf][off]) = vreg[i];
-    }
-  };
-
-  const int ntiles = (n + kBC - 1) / kBC;
-  gload(0);
-  swrite(0);
-  __syncthreads();
 
   // transposed-read addressing for V^T fragments (fixed per lane)
   const int g = lane >> 4;
@@ -134,95 +125,97 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
   const int tr_row = 4 * hi + (jj >> 2);
   const int tr_col = (g & 1) * 16 + 4 * (jj & 3);
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int j0 = t * kBC;
-    if (t + 1 < ntiles) gload(j0 + kBC);
-    const bf16* ks = sK[buf];
-    const bf16* vs = sV[buf];
-
-    // S^T = K Q^T: lane holds query l32 and, in register r of block kb,
-    // key j0 + 32*kb + 8*(r/4) + 4*hi + r%4
-    f32x16 s[QB][KB];
+  // One 32-key block: scores, online softmax, P V.
+  auto block = [&](const bf16* ks, const bf16* vs, int sb, int j0, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
+    f32x16 s[QB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[qb][kb] = f32x16{};
+    for (int dk = 0; dk < DK; ++dk) {
+      const bf16x8 a = lds_read_b128(ks + swz_off<D>(sb * 32 + l32, dk * 16 + 8 * hi));
 #pragma unroll
-      for (int dk = 0; dk < DK; ++dk) {
-        const bf16x8 a = lds_read_b128(ks + swz_off<D>(kb * 32 + l32, dk * 16 + 8 * hi));
+      for (int qb = 0; qb < QB; ++qb) s[qb] = mfma32x32x16(a, qf[qb][dk], s[qb]);
+    }
+    if constexpr (kMasked) {  // keys beyond n get no weight
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32x32x16(a, qf[qb][dk], s[qb][kb]);
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + sb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (key >= n) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) s[qb][r] = -INFINITY;
+        }
       }
     }
-    if (j0 + kBC > n) {  // ragged last tile: keys beyond n get no weight
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key >= n) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[qb][kb][r] = -INFINITY;
-          }
-        }
-    }
-
-    // online softmax; P^T fragments for the PV MFMA: chunk c, element e is
-    // register 8*(c%2) + e of block c/2
-    bf16x8 pf[QB][NC];
+    // P^T fragments: chunk c (keys 16c..16c+15 of the block), element e is register 8c + e
+    bf16x8 pf[QB][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = s[qb][0][0];
+      float mx = fmaxf(s[qb][0], s[qb][1]);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[qb][r]);
+      mx = pair_max32(mx);
+      m_run[qb] = fmaxf(m_run[qb], mx);
+      const float target = m_run[qb] * C;
+      if (wave_any(target > ref[qb] + kRefSlack)) {
+        const float alpha = fast_exp2(ref[qb] - target);  // 0 on the first block
+        ref[qb] = target;
+        l_run[qb] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-      mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_run[qb], mx);
-      const float mC = m_new * C;
-      // rescale by the ratio of the rounded references, so that all weights in
-      // l and acc stay relative to the same mC
-      const float alpha = fast_exp2(mC_run[qb] - mC);
+        for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
+      }
+      const float R = ref[qb];
       float ls = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(s[qb][kb][r], C, -mC));
-          ls += p;
-          pf[qb][2 * kb + (r >> 3)][r & 7] = (bf16)p;
-        }
-      l_run[qb] = l_run[qb] * alpha + ls;
-      m_run[qb] = m_new;
-      mC_run[qb] = mC;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(s[qb][r], C, -R));
+        ls += p;
+        pf[qb][r >> 3][r & 7] = (bf16)p;
+      }
+      l_run[qb] += ls;
     }
-
-    // O^T += V^T P^T
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
+    for (int c = 0; c < 2; ++c) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int col = db * 32 + tr_col;
-        const bf16x4 lo = lds_read_tr16(vs + swz_off<D>(c * 16 + tr_row, col));
-        const bf16x4 up = lds_read_tr16(vs + swz_off<D>(c * 16 + 8 + tr_row, col));
-        const bf16x8 a = cat(lo, up);
+        const int r0 = sb * 32 + c * 16 + tr_row;
+        const bf16x8 a = cat(lds_read_tr16(vs + swz_off<D>(r0, col)),
+                             lds_read_tr16(vs + swz_off<D>(r0 + 8, col)));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32x32x16(a, pf[qb][c], acc[qb][db]);
       }
     }
+  };
 
-    if (t + 1 < ntiles) swrite(buf ^ 1);
+  const int ntiles = (n + BC - 1) / BC;
+  issue(0, 0);
+  wait_all();
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const int j0 = t * BC;
+    if (t + 1 < ntiles) issue(buf ^ 1, j0 + BC);
+    const bf16* ks = sK[buf];
+    const bf16* vs = sV[buf];
+    if (j0 + BC <= n) {
+#pragma unroll 1
+      for (int sb = 0; sb < SB; ++sb) block(ks, vs, sb, j0, std::false_type{});
+    } else {  // ragged last tile
+      for (int sb = 0; sb < SB; ++sb) {
+        if (j0 + sb * 32 >= n) break;
+        block(ks, vs, sb, j0, std::true_type{});
+      }
+    }
+    wait_all();
     __syncthreads();
   }
 
-  // epilogue: O = acc / l, written once; statistics in natural units
+  // epilogue: O = acc / l, written once; statistics for the exact maximum
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = q0 + qb * 32 + l32;
-    const float l_tot = l_run[qb] + xor32(l_run[qb]);
+    const float l_tot = pair_sum32(l_run[qb]);
     const float inv = 1.f / l_tot;
     if (row < n) {
       bf16* orow = O + base + (int64_t)row * D;
@@ -236,18 +229,17 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
           *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * r4 + 4 * hi) = w;
         }
       if (Mx != nullptr && hi == 0) {
-        // The weights summed in l_tot are 2^eps times exp(s - m), where
-        // eps = m*C - fl(m*C) is the rounding residual of the reference
-        // (exact through one FMA); report l for the exact maximum.
-        const float eps = __builtin_fmaf(m_run[qb], C, -mC_run[qb]);
+        // l_tot sums exp2(x*C - R) = exp(s - m) * 2^(m*C - R); m*C - R is
+        // formed exactly by one FMA
+        const float shift = __builtin_fmaf(m_run[qb], C, -ref[qb]);
         Mx[(int64_t)bh * n + row] = m_run[qb] * scale;
-        Ls[(int64_t)bh * n + row] = l_tot * fast_exp2(-eps);
+        Ls[(int64_t)bh * n + row] = l_tot * fast_exp2(-shift);
       }
     }
   }
 }
 
-template <int D, int QB>
+template <int D, int QB, int BC>
 hipError_t launch(int64_t BH, int n, const void* q, const void* k, const void* v, void* o,
                   float* m, float* l, hipStream_t stream) {
   constexpr int kBQ = kWaves * QB * 32;
@@ -255,7 +247,7 @@ hipError_t launch(int64_t BH, int n, const void* q, const void* k, const void* v
   const int64_t total = BH * qtiles;
   const float scale = 1.0f / sqrtf((float)D);
   const float C = kLog2e * scale;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB>), dim3((unsigned)total), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BC>), dim3((unsigned)total), dim3(kThreads), 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, m, l, n, qtiles,
                      (int)total, C, scale);
   return hipGetLastError();
@@ -265,8 +257,8 @@ hipError_t launch(int64_t BH, int n, const void* q, const void* k, const void* v
 
 hipError_t launch_fwd_bf16(int d, int64_t BH, int n, const void* q, const void* k, const void* v,
                            void* o, float* m, float* l, hipStream_t stream) {
-  if (d == 64) return launch<64, 2>(BH, n, q, k, v, o, m, l, stream);
-  return launch<128, 1>(BH, n, q, k, v, o, m, l, stream);
+  if (d == 64) return launch<64, 2, 128>(BH, n, q, k, v, o, m, l, stream);
+  return launch<128, 1, 64>(BH, n, q, k, v, o, m, l, stream);
 }
 
 }  // namespace mea

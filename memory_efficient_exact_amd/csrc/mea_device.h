@@ -84,12 +84,37 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
 }
 
 // ---------------------------------------------------------------- wave helpers
-// value from lane l ^ 32
+// value from lane l ^ 32 (through LDS permute; used off the hot path)
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// v_permlane32_swap exchanges the upper half of one operand with the lower
+// half of the other; swapping x with itself leaves lane l holding the pair
+// {x[l % 32], x[32 + l % 32]} across the two results, whichever way round.
+// Max and sum of the pair are therefore identical (bitwise) in lanes l, l^32.
+__device__ __forceinline__ float pair_max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// true in every lane when the predicate holds in any lane of the wave
+__device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
+
+// Direct global->LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's 16 bytes land at lds_base + 16*l, where lds_base is uniform across
+// the wave. Completion is tracked by the vector-memory counter.
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (MEA_LDS void*)((uintptr_t)lds_base), 16, 0, 0);
+}
+// wait for every outstanding memory operation of this wave
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Global->LDS/row-major block index remap. The hardware hands consecutive
+// Workgroup index remap. The hardware hands consecutive
 // workgroup ids to the 8 XCDs in turn; remapping makes the ids that run on
 // one XCD consecutive in the logical order, so the query tiles of one head
 // (which stream the same K and V) share that XCD's L2.
