@@ -12,8 +12,8 @@
 // Layout of the work (per workgroup of 4 waves, two workgroups per CU):
 //  * each wave owns QB blocks of 32 query rows; the workgroup owns 4*QB*32;
 //  * K and V tiles of BC keys are copied straight from HBM into LDS
-//    (global_load_lds, no register staging), double-buffered, with the
-//    16-byte chunks of each row swizzled (see mea_device.h);
+//    (global_load_lds, no register staging), double-buffered, in a padded
+//    row-major layout (see Padded in mea_device.h);
 //  * scores are formed transposed, S^T = K Q^T, on 32x32x16 bf16 MFMA, so
 //    that each lane holds one query's scores for 16 keys per 32-key block:
 //    the row maximum is a register reduction plus one v_permlane32_swap, and
@@ -52,15 +52,21 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   constexpr int DK = D / 16;             // k-steps of the score MFMA
   constexpr int DB = D / 32;             // 32-wide output column blocks
   constexpr int SB = BC / 32;            // 32-key blocks per LDS tile
-  constexpr int kTile = BC * D;          // elements per K or V tile
-  constexpr int kBlocks = kTile / 512;   // 1 KiB DMA blocks per tile
-  constexpr int kBPW = kBlocks / kWaves; // DMA blocks per wave per tile
-  constexpr int RPB = 512 / D;           // rows per DMA block
-  constexpr int LPR = D / 8;             // lanes per row in a DMA block
-  static_assert(kBPW * kWaves == kBlocks, "tile split");
+  using L = Padded<D>;
+  constexpr int RS = L::kRowElems;        // LDS row stride (elements)
+  constexpr int SPR = L::kSlotsPerRow;    // 16-byte slots per LDS row
+  constexpr int kTile = BC * RS;          // elements per K or V tile in LDS
+  constexpr int NBLK = BC * SPR / 64;     // 1 KiB DMA blocks per tile
+  constexpr int BPW = (NBLK + kWaves - 1) / kWaves;
+  static_assert(NBLK * 64 == BC * SPR, "tile must be whole DMA blocks");
 
-  __shared__ __attribute__((aligned(1024))) bf16 sK[2][kTile];
-  __shared__ __attribute__((aligned(1024))) bf16 sV[2][kTile];
+  // two named buffers per operand (not one array indexed by a loop
+  // variable), so the compiler can see that reads of the current tile never
+  // alias the DMA into the other one and does not wait for that DMA
+  __shared__ __attribute__((aligned(1024))) bf16 sK0[kTile];
+  __shared__ __attribute__((aligned(1024))) bf16 sK1[kTile];
+  __shared__ __attribute__((aligned(1024))) bf16 sV0[kTile];
+  __shared__ __attribute__((aligned(1024))) bf16 sV1[kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -102,28 +108,39 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
   }
 
-  // DMA of the K and V tile starting at key j0 into buffer `buf`. Block b of
-  // the tile holds rows b*RPB.. ; lane l fills physical chunk l%LPR of row
-  // b*RPB + l/LPR, so it fetches the logical chunk that the swizzle puts
-  // there. Rows past n repeat row n-1 (their scores are masked to -inf).
-  auto issue = [&](int buf, int j0) {
+  // DMA of the K and V tile starting at key j0. Block b of a tile covers
+  // 16-byte LDS slots 64b..64b+63; slot s is row s / SPR, column chunk
+  // s % SPR of the padded layout. Pad slots fetch a duplicate of the row's
+  // first chunk (never read). Rows past n repeat row n-1 (their scores are
+  // masked to -inf, and their weights are exactly 0).
+  int dma_row[BPW], dma_col[BPW];
 #pragma unroll
-    for (int i = 0; i < kBPW; ++i) {
-      const int b = wave * kBPW + i;
-      const int r = b * RPB + lane / LPR;
-      const int ch = swz_chunk<D>(r, lane % LPR);
-      const int src = min(j0 + r, n - 1);
-      const int64_t off = (int64_t)src * D + ch * 8;
-      dma16(Kh + off, &sK[buf][b * 512]);
-      dma16(Vh + off, &sV[buf][b * 512]);
+  for (int i = 0; i < BPW; ++i) {
+    const int slot = (wave + kWaves * i) * 64 + lane;
+    const int r = slot / SPR;
+    const int c = slot - r * SPR;
+    dma_row[i] = r;
+    dma_col[i] = (c == SPR - 1 ? 0 : c) * 8;
+  }
+  auto issue = [&](bf16* kdst, bf16* vdst, int j0) {
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const int b = wave + kWaves * i;
+      if (b < NBLK) {
+        const int src = min(j0 + dma_row[i], n - 1);
+        const int64_t off = (int64_t)src * D + dma_col[i];
+        dma16(Kh + off, kdst + b * 512);
+        dma16(Vh + off, vdst + b * 512);
+      }
     }
   };
 
-  // transposed-read addressing for V^T fragments (fixed per lane)
+  // per-lane LDS offsets: K rows for the score MFMA, and the transposed-read
+  // pattern for V^T fragments (row 4*hi + jj/4, column 16*(g%2) + 4*(jj%4))
   const int g = lane >> 4;
   const int jj = lane & 15;
-  const int tr_row = 4 * hi + (jj >> 2);
-  const int tr_col = (g & 1) * 16 + 4 * (jj & 3);
+  const int k_lane = L::off(l32, 8 * hi);
+  const int v_lane = L::off(4 * hi + (jj >> 2), (g & 1) * 16 + 4 * (jj & 3));
 
   // One 32-key block: scores, online softmax, P V.
   auto block = [&](const bf16* ks, const bf16* vs, int sb, int j0, auto masked_tag) {
@@ -133,7 +150,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
 #pragma unroll
     for (int dk = 0; dk < DK; ++dk) {
-      const bf16x8 a = lds_read_b128(ks + swz_off<D>(sb * 32 + l32, dk * 16 + 8 * hi));
+      const bf16x8 a = lds_read_b128(ks + k_lane + L::off(sb * 32, dk * 16));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) s[qb] = mfma32x32x16(a, qf[qb][dk], s[qb]);
     }
@@ -178,10 +195,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int col = db * 32 + tr_col;
-        const int r0 = sb * 32 + c * 16 + tr_row;
-        const bf16x8 a = cat(lds_read_tr16(vs + swz_off<D>(r0, col)),
-                             lds_read_tr16(vs + swz_off<D>(r0 + 8, col)));
+        const bf16* vp = vs + v_lane + L::off(sb * 32 + c * 16, db * 32);
+        const bf16x8 a = cat(lds_read_tr16(vp), lds_read_tr16(vp + 8 * RS));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32x32x16(a, pf[qb][c], acc[qb][db]);
       }
@@ -189,15 +204,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   };
 
   const int ntiles = (n + BC - 1) / BC;
-  issue(0, 0);
-  wait_all();
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  // one tile: prefetch the next tile into (kn, vn) while computing on (ks, vs)
+  auto step = [&](const bf16* ks, const bf16* vs, bf16* kn, bf16* vn, int t) {
     const int j0 = t * BC;
-    if (t + 1 < ntiles) issue(buf ^ 1, j0 + BC);
-    const bf16* ks = sK[buf];
-    const bf16* vs = sV[buf];
+    if (t + 1 < ntiles) issue(kn, vn, j0 + BC);
     if (j0 + BC <= n) {
 #pragma unroll 1
       for (int sb = 0; sb < SB; ++sb) block(ks, vs, sb, j0, std::false_type{});
@@ -209,6 +219,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     }
     wait_all();
     __syncthreads();
+  };
+  issue(sK0, sV0, 0);
+  wait_all();
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    step(sK0, sV0, sK1, sV1, t);
+    if (t + 1 < ntiles) step(sK1, sV1, sK0, sV0, t + 1);
   }
 
   // epilogue: O = acc / l, written once; statistics for the exact maximum

@@ -64,6 +64,19 @@ __device__ __forceinline__ int swz_off(int row, int col) {
   return row * D + swz_chunk<D>(row, col >> 3) * 8 + (col & 7);
 }
 
+// Padded row-major bf16 tile: each row of D elements is followed by 16 bytes
+// of padding, so row r starts at byte r*(2D + 16). For D = 64 (144-byte rows)
+// consecutive rows start 36 banks apart: 16 rows read at the same 16-byte
+// column cover all 64 banks once, and the 4-row x 32-byte footprint of a
+// transposed read by 16 lanes is conflict-free as well. Every address is a
+// per-lane base plus compile-time offsets, with no swizzle arithmetic.
+template <int D>
+struct Padded {
+  static constexpr int kRowElems = D + 8;           // row stride in elements
+  static constexpr int kSlotsPerRow = D / 8 + 1;    // 16-byte slots per row (last = pad)
+  __device__ static constexpr int off(int row, int col) { return row * kRowElems + col; }
+};
+
 __device__ __forceinline__ bf16x8 lds_read_b128(const bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
@@ -74,8 +87,7 @@ __device__ __forceinline__ bf16x8 lds_read_b128(const bf16* p) {
 // If lane j of a group addresses row (base + j/4), columns c0 + 4*(j%4)..+3
 // of a row-major tile, output lane i holds rows base..base+3 of column c0 + i.
 __device__ __forceinline__ bf16x4 lds_read_tr16(const bf16* p) {
-  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (MEA_LDS i16x4*)((MEA_LDS char*)((uintptr_t)p)));
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MEA_LDS i16x4*)(p));
   return __builtin_bit_cast(bf16x4, v);
 }
 
@@ -107,7 +119,7 @@ __device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
 // lane l's 16 bytes land at lds_base + 16*l, where lds_base is uniform across
 // the wave. Completion is tracked by the vector-memory counter.
 __device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (MEA_LDS void*)((uintptr_t)lds_base), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(gsrc, (MEA_LDS void*)(lds_base), 16, 0, 0);
 }
 // wait for every outstanding memory operation of this wave
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
