@@ -135,18 +135,21 @@ def main():
     log(f"step {ms:.3f} ms | fwd {f_avg:.3f} ms ({fwd_tf:.1f} TFLOP/s, "
         f"{100 * fwd_tf / PEAK_BF16_TFLOPS:.1f}% of peak) | bwd {b_avg:.3f} ms ({bwd_tf:.1f} TFLOP/s)")
 
-    # Roofline of the forward kernel (one launch per attn_fwd call, timed by the
-    # events around that call on the launch stream).
+    # Roofline of the dominant kernel, bwd_main_kernel<64> (the backward's
+    # MFMA work: algorithmically 10*B*H*n^2*d flops per launch). Its average
+    # launch duration is taken from HIP events around each attn_bwd call on the
+    # launch stream; that call also runs the O(n*d) row pass (a few
+    # microseconds), so the figure is a slight underestimate.
     roofline = {
-        "kernel": "fwd_bf16_kernel<64,2>",
+        "kernel": "bwd_main_kernel<64>",
         "bound": "mfma",
-        "achieved": fwd_tf,
+        "achieved": bwd_tf,
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
-        "frac": fwd_tf / PEAK_BF16_TFLOPS,
+        "frac": bwd_tf / PEAK_BF16_TFLOPS,
         "traffic": None,
-        "avg_launch_ms": f_avg,
-        "flops_per_launch": fwd_flops,
+        "avg_launch_ms": b_avg,
+        "flops_per_launch": bwd_flops,
     }
     out = {
         "metric": METRIC,

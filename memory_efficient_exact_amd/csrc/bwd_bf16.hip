@@ -3,23 +3,33 @@
 // "Self-attention Does Not Need O(n^2) Memory" (abstract; 方法详解; English
 // digest method bullets) differentiates the chunked forward by recomputing
 // each chunk's intermediates instead of storing them. Here the forward saves
-// only two fp32 numbers per query row (row max m_i and row sum l_i); every
-// kernel below rebuilds the probability tile
+// only two fp32 numbers per query row (row max m_i and row sum l_i); the
+// kernels below rebuild the probability tile
 //     P_ij = exp(s_ij - m_i) / l_i = exp2(x_ij * log2(e)/sqrt(d) - lse2_i),
 //     lse2_i = m_i * log2(e) + log2(l_i),   x_ij = q_i . k_j,
 // from Q and K on the fly. The pages print no gradient formulas; the textbook
 // softmax Jacobian is used: dV = P^T dO, dP = dO V^T, D_i = dO_i . O_i,
 // dS = P * (dP - D), dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d).
 //
-// Three kernels on the caller's stream:
-//  1. bwd_rows:  D_i and lse2_i for every row, into the workspace.
-//  2. bwd_dkdv:  one workgroup per 128-key tile (32 keys per wave, K and V of
-//     those keys in registers); sweeps all query tiles (Q, dO, lse2, D staged
-//     in LDS, double-buffered) accumulating dV^T and dK^T in registers.
-//  3. bwd_dq:    one workgroup per query tile (32 queries per wave, Q and dO
-//     in registers); sweeps all key tiles (K, V in LDS) accumulating dQ^T.
+// Two launches on the caller's stream:
+//  1. bwd_rows: D_i and lse2_i for every row, into the workspace (reads O,
+//     dO, m, l once; a few microseconds).
+//  2. bwd_main: one grid holding two kinds of workgroup.
+//     * dK/dV workgroups own 128 keys (32 per wave, K and V of those keys in
+//       registers) and sweep every query tile of 64 rows (Q, dO, lse2, D
+//       copied into LDS by DMA, double-buffered), accumulating dV^T and dK^T
+//       in registers: per tile S = Q K^T, dP = dO V^T (lane = key), then
+//       dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T from transposed LDS
+//       reads.
+//     * dQ workgroups own 128 queries (32 per wave, Q and dO in registers)
+//       and sweep every key tile of 64 keys (K, V in LDS), accumulating dQ^T:
+//       S^T = K Q^T, dP^T = V dO^T (lane = query), dQ^T += K^T dS^T.
+//     The dK/dV workgroups come first in the grid (they carry more work), the
+//     dQ workgroups fill the machine behind them.
 // No probability or score array is written to memory; dQ, dK and dV are each
-// written once, so the result does not depend on scheduling (deterministic).
+// written once by one workgroup, so results do not depend on scheduling.
+#include <type_traits>
+
 #include "mea_device.h"
 #include "mea_launch.h"
 
@@ -28,6 +38,10 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsKV = kWaves * 32;  // keys per dK/dV workgroup
+constexpr int kRowsQ = kWaves * 32;   // queries per dQ workgroup
+constexpr int kTileQ = 64;            // query rows per staged tile (dK/dV role)
+constexpr int kTileK = 64;            // key rows per staged tile (dQ role)
 
 // ------------------------------------------------------------ 1. row terms
 // One wave per 8 rows (d=64) / 4 rows (d=128): lanes read 16 bytes of O and
@@ -56,54 +70,63 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(
   }
 }
 
-// ------------------------------------------------------------ 2. dK and dV
-constexpr int kBQ2 = 64;  // query rows per staged tile
+// ------------------------------------------------------------ 2. main kernel
+struct BwdArgs {
+  const bf16* Q;
+  const bf16* K;
+  const bf16* V;
+  const bf16* dO;
+  const float* Dv;
+  const float* Lse2;
+  bf16* dQ;
+  bf16* dK;
+  bf16* dV;
+  int n;
+  int tiles_kv;   // dK/dV workgroups per (b, h)
+  int tiles_q;    // dQ workgroups per (b, h)
+  int total_kv;   // dK/dV workgroups in the grid
+  int total_q;    // dQ workgroups in the grid
+  float C;        // log2(e) / sqrt(d)
+  float scale;    // 1 / sqrt(d)
+};
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ Dv, const float* __restrict__ Lse2,
-    bf16* __restrict__ dK, bf16* __restrict__ dV, int n, int ktiles, int total, float C,
-    float scale) {
-  constexpr int kBK = kWaves * 32;  // keys per workgroup
+struct BwdShared {
+  using TQ = TileDma<D, kTileQ, kWaves>;
+  using TK = TileDma<D, kTileK, kWaves>;
+  static_assert(TQ::kElems == TK::kElems, "both roles share the LDS arrays");
+  static constexpr int kElems = TQ::kElems;
+};
+
+// --- dK / dV role -----------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void dkdv_role(const BwdArgs& a, int wg, bf16* s0, bf16* s1, bf16* s2,
+                                          bf16* s3, float* f0, float* f1) {
+  using L = Padded<D>;
+  using TQ = TileDma<D, kTileQ, kWaves>;
+  constexpr int RS = L::kRowElems;
   constexpr int DK = D / 16;
   constexpr int DB = D / 32;
-  constexpr int NC = kBQ2 / 16;   // 16-query chunks per staged tile
-  constexpr int QBT = kBQ2 / 32;  // 32-query blocks per staged tile
-  constexpr int kTile = kBQ2 * D;
-  constexpr int kCPR = D / 8;
-  constexpr int kLoads = kTile / 8 / kThreads;
-  static_assert(kLoads * 8 * kThreads == kTile, "tile split");
+  constexpr int NC = kTileQ / 16;  // 16-query chunks per tile
+  constexpr int QBT = kTileQ / 32; // 32-query blocks per tile
 
-  __shared__ __attribute__((aligned(16))) bf16 sQ[2][kTile];
-  __shared__ __attribute__((aligned(16))) bf16 sO[2][kTile];  // dO tile
-  __shared__ __attribute__((aligned(16))) float sL[2][kBQ2];  // lse2
-  __shared__ __attribute__((aligned(16))) float sD[2][kBQ2];  // D
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
-
-  const int tile = xcd_remap(blockIdx.x, total);
-  const int bh = tile / ktiles;
-  const int kt = tile - bh * ktiles;
+  const int n = a.n;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int tile = xcd_remap(wg, a.total_kv);
+  const int bh = tile / a.tiles_kv;
+  const int kt = tile - bh * a.tiles_kv;
   const int64_t base = (int64_t)bh * n * D;
   const int64_t rbase = (int64_t)bh * n;
-  const int key = kt * kBK + wave * 32 + l32;  // this lane's key (column of S)
+  const int key = kt * kRowsKV + wave * 32 + l32;  // this lane's key (column of S)
 
   // K and V of this wave's 32 keys: B operands of S = Q K^T and dP = dO V^T
   bf16x8 kf[DK], vf[DK];
+  const int krow = min(key, n - 1);
 #pragma unroll
   for (int dk = 0; dk < DK; ++dk) {
-    if (key < n) {
-      kf[dk] = *reinterpret_cast<const bf16x8*>(K + base + (int64_t)key * D + dk * 16 + 8 * hi);
-      vf[dk] = *reinterpret_cast<const bf16x8*>(V + base + (int64_t)key * D + dk * 16 + 8 * hi);
-    } else {
-      kf[dk] = bf16x8{};
-      vf[dk] = bf16x8{};
-    }
+    kf[dk] = *reinterpret_cast<const bf16x8*>(a.K + base + (int64_t)krow * D + dk * 16 + 8 * hi);
+    vf[dk] = *reinterpret_cast<const bf16x8*>(a.V + base + (int64_t)krow * D + dk * 16 + 8 * hi);
   }
   f32x16 accV[DB], accK[DB];  // dV^T, dK^T: register r -> column 32*db + 8*(r/4) + 4*hi + r%4
 #pragma unroll
@@ -112,85 +135,49 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
     accK[db] = f32x16{};
   }
 
-  u32x4 qreg[kLoads], oreg[kLoads];
-  float lreg = 0.f, dreg = 0.f;
-  auto gload = [&](int i0) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c / kCPR;
-      const int ch = c - r * kCPR;
-      if (i0 + r < n) {
-        const int64_t off = base + (int64_t)(i0 + r) * D + ch * 8;
-        qreg[i] = *reinterpret_cast<const u32x4*>(Q + off);
-        oreg[i] = *reinterpret_cast<const u32x4*>(dO + off);
-      } else {
-        qreg[i] = u32x4{};
-        oreg[i] = u32x4{};
-      }
-    }
-    if (tid < kBQ2) {
-      const bool ok = i0 + tid < n;
-      lreg = ok ? Lse2[rbase + i0 + tid] : INFINITY;  // padding rows get P = 0
-      dreg = ok ? Dv[rbase + i0 + tid] : 0.f;
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c / kCPR;
-      const int ch = c - r * kCPR;
-      const int off = r * D + swz_chunk<D>(r, ch) * 8;
-      *reinterpret_cast<u32x4*>(&sQ[buf][off]) = qreg[i];
-      *reinterpret_cast<u32x4*>(&sO[buf][off]) = oreg[i];
-    }
-    if (tid < kBQ2) {
-      sL[buf][tid] = lreg;
-      sD[buf][tid] = dreg;
+  TQ dma;
+  dma.init(wave, lane);
+  // lse2 and D of a query tile: 64 floats each, one 4-byte DMA per lane
+  auto issue = [&](bf16* qdst, bf16* odst, float* fdst, int i0) {
+    dma.issue(a.Q + base, i0, n, qdst);
+    dma.issue(a.dO + base, i0, n, odst);
+    if (wave == kWaves - 1) {
+      const int r = min(i0 + lane, n - 1);
+      dma4(a.Lse2 + rbase + r, fdst);
+      dma4(a.Dv + rbase + r, fdst + kTileQ);
     }
   };
 
-  const int g = lane >> 4;
-  const int jj = lane & 15;
-  const int tr_row = 4 * hi + (jj >> 2);
-  const int tr_col = (g & 1) * 16 + 4 * (jj & 3);
+  const int g = lane >> 4, jj = lane & 15;
+  const int a_lane = L::off(l32, 8 * hi);  // 16-byte row reads (A operands of S, dP)
+  const int t_lane = L::off(4 * hi + (jj >> 2), (g & 1) * 16 + 4 * (jj & 3));  // transposed reads
 
-  const int ntiles = (n + kBQ2 - 1) / kBQ2;
-  gload(0);
-  swrite(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) gload((t + 1) * kBQ2);
-    const bf16* qs = sQ[buf];
-    const bf16* os = sO[buf];
-    const float* ls = sL[buf];
-    const float* dsv = sD[buf];
-
-    bf16x8 pf[NC], sf[NC];  // P and dS as B operands: chunk c element e <-> query 16c + 8(e/4) + 4hi + e%4
+  auto tile_body = [&](const bf16* qs, const bf16* os, const float* fs, int i0, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
+    bf16x8 pf[NC], sf[NC];  // P and dS: chunk c element e <-> query 16c + 8(e/4) + 4hi + e%4
 #pragma unroll
     for (int qb = 0; qb < QBT; ++qb) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int dk = 0; dk < DK; ++dk) {
-        const int off = swz_off<D>(qb * 32 + l32, dk * 16 + 8 * hi);
+        const int off = a_lane + L::off(qb * 32, dk * 16);
         s = mfma32x32x16(lds_read_b128(qs + off), kf[dk], s);
         dp = mfma32x32x16(lds_read_b128(os + off), vf[dk], dp);
       }
-      // lane holds key `key`; register r holds query row 32*qb + 8*(r/4) + 4*hi + r%4
+      // lane holds key `key`; register r holds query row i0 + 32*qb + 8*(r/4) + 4*hi + r%4
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 lse = *reinterpret_cast<const f32x4*>(ls + qb * 32 + 8 * r4 + 4 * hi);
-        const f32x4 dd = *reinterpret_cast<const f32x4*>(dsv + qb * 32 + 8 * r4 + 4 * hi);
+        const f32x4 lse = *reinterpret_cast<const f32x4*>(fs + qb * 32 + 8 * r4 + 4 * hi);
+        const f32x4 dd = *reinterpret_cast<const f32x4*>(fs + kTileQ + qb * 32 + 8 * r4 + 4 * hi);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
-          const float p = fast_exp2(__builtin_fmaf(s[r], C, -lse[e]));
-          const float dsc = p * (dp[r] - dd[e]);
+          float p = fast_exp2(__builtin_fmaf(s[r], a.C, -lse[e]));
+          if constexpr (kMasked) {
+            if (i0 + qb * 32 + 8 * r4 + 4 * hi + e >= n) p = 0.f;  // padding query rows
+          }
           pf[2 * qb + (r >> 3)][r & 7] = (bf16)p;
-          sf[2 * qb + (r >> 3)][r & 7] = (bf16)dsc;
+          sf[2 * qb + (r >> 3)][r & 7] = (bf16)(p * (dp[r] - dd[e]));
         }
       }
     }
@@ -199,22 +186,36 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
     for (int c = 0; c < NC; ++c) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int col = db * 32 + tr_col;
-        const int o0 = swz_off<D>(c * 16 + tr_row, col);
-        const int o1 = swz_off<D>(c * 16 + 8 + tr_row, col);
-        const bf16x8 ao = cat(lds_read_tr16(os + o0), lds_read_tr16(os + o1));
-        const bf16x8 aq = cat(lds_read_tr16(qs + o0), lds_read_tr16(qs + o1));
+        const int off = t_lane + L::off(c * 16, db * 32);
+        const bf16x8 ao = cat(lds_read_tr16(os + off), lds_read_tr16(os + off + 8 * RS));
+        const bf16x8 aq = cat(lds_read_tr16(qs + off), lds_read_tr16(qs + off + 8 * RS));
         accV[db] = mfma32x32x16(ao, pf[c], accV[db]);
         accK[db] = mfma32x32x16(aq, sf[c], accK[db]);
       }
     }
-    if (t + 1 < ntiles) swrite(buf ^ 1);
+  };
+
+  const int ntiles = (n + kTileQ - 1) / kTileQ;
+  auto step = [&](const bf16* qs, const bf16* os, const float* fs, bf16* qn, bf16* on, float* fn,
+                  int t) {
+    const int i0 = t * kTileQ;
+    if (t + 1 < ntiles) issue(qn, on, fn, i0 + kTileQ);
+    if (i0 + kTileQ <= n) tile_body(qs, os, fs, i0, std::false_type{});
+    else tile_body(qs, os, fs, i0, std::true_type{});
+    wait_all();
     __syncthreads();
+  };
+  issue(s0, s1, f0, 0);
+  wait_all();
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    step(s0, s1, f0, s2, s3, f1, t);
+    if (t + 1 < ntiles) step(s2, s3, f1, s0, s1, f0, t + 1);
   }
 
   if (key < n) {
-    bf16* vrow = dV + base + (int64_t)key * D;
-    bf16* krow = dK + base + (int64_t)key * D;
+    bf16* vrow = a.dV + base + (int64_t)key * D;
+    bf16* krow_out = a.dK + base + (int64_t)key * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -223,126 +224,73 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           wv[e] = (bf16)accV[db][4 * r4 + e];
-          wk[e] = (bf16)(accK[db][4 * r4 + e] * scale);
+          wk[e] = (bf16)(accK[db][4 * r4 + e] * a.scale);
         }
         *reinterpret_cast<bf16x4*>(vrow + db * 32 + 8 * r4 + 4 * hi) = wv;
-        *reinterpret_cast<bf16x4*>(krow + db * 32 + 8 * r4 + 4 * hi) = wk;
+        *reinterpret_cast<bf16x4*>(krow_out + db * 32 + 8 * r4 + 4 * hi) = wk;
       }
   }
 }
 
-// ------------------------------------------------------------ 3. dQ
-constexpr int kBC3 = 64;  // keys per staged tile
-
+// --- dQ role ------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ Dv, const float* __restrict__ Lse2,
-    bf16* __restrict__ dQ, int n, int qtiles, int total, float C, float scale) {
-  constexpr int kBQ = kWaves * 32;
+__device__ __forceinline__ void dq_role(const BwdArgs& a, int wg, bf16* s0, bf16* s1, bf16* s2,
+                                        bf16* s3) {
+  using L = Padded<D>;
+  using TK = TileDma<D, kTileK, kWaves>;
+  constexpr int RS = L::kRowElems;
   constexpr int DK = D / 16;
   constexpr int DB = D / 32;
-  constexpr int KB = kBC3 / 32;
-  constexpr int NC = kBC3 / 16;
-  constexpr int kTile = kBC3 * D;
-  constexpr int kCPR = D / 8;
-  constexpr int kLoads = kTile / 8 / kThreads;
-  static_assert(kLoads * 8 * kThreads == kTile, "tile split");
+  constexpr int KB = kTileK / 32;
+  constexpr int NC = kTileK / 16;
 
-  __shared__ __attribute__((aligned(16))) bf16 sK[2][kTile];
-  __shared__ __attribute__((aligned(16))) bf16 sV[2][kTile];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
-
-  const int tile = xcd_remap(blockIdx.x, total);
-  const int bh = tile / qtiles;
-  const int qt = tile - bh * qtiles;
+  const int n = a.n;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int tile = xcd_remap(wg, a.total_q);
+  const int bh = tile / a.tiles_q;
+  const int qt = tile - bh * a.tiles_q;
   const int64_t base = (int64_t)bh * n * D;
-  const int row = qt * kBQ + wave * 32 + l32;  // this lane's query
+  const int row = qt * kRowsQ + wave * 32 + l32;  // this lane's query
+  const int qrow = min(row, n - 1);
 
   bf16x8 qf[DK], of[DK];  // B operands of S^T = K Q^T and dP^T = V dO^T
 #pragma unroll
   for (int dk = 0; dk < DK; ++dk) {
-    if (row < n) {
-      qf[dk] = *reinterpret_cast<const bf16x8*>(Q + base + (int64_t)row * D + dk * 16 + 8 * hi);
-      of[dk] = *reinterpret_cast<const bf16x8*>(dO + base + (int64_t)row * D + dk * 16 + 8 * hi);
-    } else {
-      qf[dk] = bf16x8{};
-      of[dk] = bf16x8{};
-    }
+    qf[dk] = *reinterpret_cast<const bf16x8*>(a.Q + base + (int64_t)qrow * D + dk * 16 + 8 * hi);
+    of[dk] = *reinterpret_cast<const bf16x8*>(a.dO + base + (int64_t)qrow * D + dk * 16 + 8 * hi);
   }
-  const float lse = row < n ? Lse2[(int64_t)bh * n + row] : INFINITY;
-  const float dd = row < n ? Dv[(int64_t)bh * n + row] : 0.f;
+  const float lse = a.Lse2[(int64_t)bh * n + qrow];
+  const float dd = a.Dv[(int64_t)bh * n + qrow];
 
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-  u32x4 kreg[kLoads], vreg[kLoads];
-  auto gload = [&](int j0) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c / kCPR;
-      const int ch = c - r * kCPR;
-      if (j0 + r < n) {
-        const int64_t off = base + (int64_t)(j0 + r) * D + ch * 8;
-        kreg[i] = *reinterpret_cast<const u32x4*>(K + off);
-        vreg[i] = *reinterpret_cast<const u32x4*>(V + off);
-      } else {
-        kreg[i] = u32x4{};
-        vreg[i] = u32x4{};
-      }
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c / kCPR;
-      const int ch = c - r * kCPR;
-      const int off = r * D + swz_chunk<D>(r, ch) * 8;
-      *reinterpret_cast<u32x4*>(&sK[buf][off]) = kreg[i];
-      *reinterpret_cast<u32x4*>(&sV[buf][off]) = vreg[i];
-    }
-  };
+  TK dma;
+  dma.init(wave, lane);
+  const int g = lane >> 4, jj = lane & 15;
+  const int a_lane = L::off(l32, 8 * hi);
+  const int t_lane = L::off(4 * hi + (jj >> 2), (g & 1) * 16 + 4 * (jj & 3));
 
-  const int g = lane >> 4;
-  const int jj = lane & 15;
-  const int tr_row = 4 * hi + (jj >> 2);
-  const int tr_col = (g & 1) * 16 + 4 * (jj & 3);
-
-  const int ntiles = (n + kBC3 - 1) / kBC3;
-  gload(0);
-  swrite(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int j0 = t * kBC3;
-    if (t + 1 < ntiles) gload(j0 + kBC3);
-    const bf16* ks = sK[buf];
-    const bf16* vs = sV[buf];
-
+  auto tile_body = [&](const bf16* ks, const bf16* vs, int j0, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
     bf16x8 sf[NC];  // dS^T as B operand, same chunking as P^T in the forward
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int dk = 0; dk < DK; ++dk) {
-        const int off = swz_off<D>(kb * 32 + l32, dk * 16 + 8 * hi);
+        const int off = a_lane + L::off(kb * 32, dk * 16);
         s = mfma32x32x16(lds_read_b128(ks + off), qf[dk], s);
         dp = mfma32x32x16(lds_read_b128(vs + off), of[dk], dp);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kj = j0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        float p = fast_exp2(__builtin_fmaf(s[r], C, -lse));
-        if (kj >= n) p = 0.f;
+        float p = fast_exp2(__builtin_fmaf(s[r], a.C, -lse));
+        if constexpr (kMasked) {
+          if (j0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3) >= n) p = 0.f;  // padding keys
+        }
         sf[2 * kb + (r >> 3)][r & 7] = (bf16)(p * (dp[r] - dd));
       }
     }
@@ -351,36 +299,68 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
     for (int c = 0; c < NC; ++c) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int col = db * 32 + tr_col;
-        const bf16x8 a = cat(lds_read_tr16(ks + swz_off<D>(c * 16 + tr_row, col)),
-                             lds_read_tr16(ks + swz_off<D>(c * 16 + 8 + tr_row, col)));
-        acc[db] = mfma32x32x16(a, sf[c], acc[db]);
+        const int off = t_lane + L::off(c * 16, db * 32);
+        const bf16x8 ak = cat(lds_read_tr16(ks + off), lds_read_tr16(ks + off + 8 * RS));
+        acc[db] = mfma32x32x16(ak, sf[c], acc[db]);
       }
     }
-    if (t + 1 < ntiles) swrite(buf ^ 1);
+  };
+
+  const int ntiles = (n + kTileK - 1) / kTileK;
+  auto step = [&](const bf16* ks, const bf16* vs, bf16* kn, bf16* vn, int t) {
+    const int j0 = t * kTileK;
+    if (t + 1 < ntiles) {
+      dma.issue(a.K + base, j0 + kTileK, n, kn);
+      dma.issue(a.V + base, j0 + kTileK, n, vn);
+    }
+    if (j0 + kTileK <= n) tile_body(ks, vs, j0, std::false_type{});
+    else tile_body(ks, vs, j0, std::true_type{});
+    wait_all();
     __syncthreads();
+  };
+  dma.issue(a.K + base, 0, n, s0);
+  dma.issue(a.V + base, 0, n, s1);
+  wait_all();
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    step(s0, s1, s2, s3, t);
+    if (t + 1 < ntiles) step(s2, s3, s0, s1, t + 1);
   }
 
   if (row < n) {
-    bf16* qrow = dQ + base + (int64_t)row * D;
+    bf16* qout = a.dQ + base + (int64_t)row * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         bf16x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * r4 + e] * scale);
-        *reinterpret_cast<bf16x4*>(qrow + db * 32 + 8 * r4 + 4 * hi) = w;
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * r4 + e] * a.scale);
+        *reinterpret_cast<bf16x4*>(qout + db * 32 + 8 * r4 + 4 * hi) = w;
       }
   }
+}
+
+// d = 64 fits two workgroups per CU (2 waves per SIMD, <= 256 registers);
+// d = 128 needs the full register file of one wave per SIMD.
+template <int D>
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_main_kernel(BwdArgs a) {
+  // two named buffers per staged operand (see the forward kernel)
+  __shared__ __attribute__((aligned(1024))) bf16 s0[BwdShared<D>::kElems];
+  __shared__ __attribute__((aligned(1024))) bf16 s1[BwdShared<D>::kElems];
+  __shared__ __attribute__((aligned(1024))) bf16 s2[BwdShared<D>::kElems];
+  __shared__ __attribute__((aligned(1024))) bf16 s3[BwdShared<D>::kElems];
+  __shared__ __attribute__((aligned(256))) float f0[2 * kTileQ];
+  __shared__ __attribute__((aligned(256))) float f1[2 * kTileQ];
+  const int wg = blockIdx.x;
+  if (wg < a.total_kv) dkdv_role<D>(a, wg, s0, s1, s2, s3, f0, f1);
+  else dq_role<D>(a, wg - a.total_kv, s0, s1, s2, s3);
 }
 
 template <int D>
 hipError_t launch(int64_t BH, int n, const void* q, const void* k, const void* v, const void* o,
                   const void* dO, const float* m, const float* l, void* dq, void* dk, void* dv,
                   float* ws, hipStream_t stream) {
-  const float scale = 1.0f / sqrtf((float)D);
-  const float C = kLog2e * scale;
   const int64_t rows = BH * n;
   float* Dv = ws;
   float* Lse2 = ws + rows;
@@ -392,22 +372,25 @@ hipError_t launch(int64_t BH, int n, const void* q, const void* k, const void* v
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
-    const int ktiles = (n + kWaves * 32 - 1) / (kWaves * 32);
-    const int total = (int)(BH * ktiles);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(total), dim3(kThreads), 0, stream,
-                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, Dv, Lse2,
-                       (bf16*)dk, (bf16*)dv, n, ktiles, total, C, scale);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  {
-    const int qtiles = (n + kWaves * 32 - 1) / (kWaves * 32);
-    const int total = (int)(BH * qtiles);
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(total), dim3(kThreads), 0, stream,
-                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dO, Dv, Lse2,
-                       (bf16*)dq, n, qtiles, total, C, scale);
-  }
+  BwdArgs a;
+  a.Q = (const bf16*)q;
+  a.K = (const bf16*)k;
+  a.V = (const bf16*)v;
+  a.dO = (const bf16*)dO;
+  a.Dv = Dv;
+  a.Lse2 = Lse2;
+  a.dQ = (bf16*)dq;
+  a.dK = (bf16*)dk;
+  a.dV = (bf16*)dv;
+  a.n = n;
+  a.tiles_kv = (n + kRowsKV - 1) / kRowsKV;
+  a.tiles_q = (n + kRowsQ - 1) / kRowsQ;
+  a.total_kv = (int)(BH * a.tiles_kv);
+  a.total_q = (int)(BH * a.tiles_q);
+  a.scale = 1.0f / sqrtf((float)D);
+  a.C = kLog2e * a.scale;
+  hipLaunchKernelGGL((bwd_main_kernel<D>), dim3((unsigned)(a.total_kv + a.total_q)), dim3(kThreads),
+                     0, stream, a);
   return hipGetLastError();
 }
 

@@ -121,6 +121,54 @@ __device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
 __device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (MEA_LDS void*)(lds_base), 16, 0, 0);
 }
+// Direct global->LDS copy of 4 bytes per lane (global_load_lds_dword):
+// lane l's 4 bytes land at lds_base + 4*l.
+__device__ __forceinline__ void dma4(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (MEA_LDS void*)(lds_base), 4, 0, 0);
+}
+
+// Copies a tile of ROWS consecutive rows of a row-major [*, D] bf16 array
+// into the padded LDS layout with 16-byte DMA, spread over the waves of a
+// workgroup. DMA block b covers LDS slots 64b..64b+63; slot s is row
+// s / kSlotsPerRow, chunk s % kSlotsPerRow. Pad slots fetch a duplicate of
+// the row's first chunk. Source rows at or past `n` are clamped to n - 1,
+// so every global read stays inside the tensor.
+template <int D, int ROWS, int WAVES>
+struct TileDma {
+  using L = Padded<D>;
+  static constexpr int kBlocks = ROWS * L::kSlotsPerRow / 64;
+  static constexpr int kPerWave = (kBlocks + WAVES - 1) / WAVES;
+  static_assert(kBlocks * 64 == ROWS * L::kSlotsPerRow, "tile must be whole DMA blocks");
+  static constexpr int kElems = ROWS * L::kRowElems;  // LDS elements per tile
+
+  int row[kPerWave];
+  int col[kPerWave];
+  int wave;
+
+  __device__ void init(int wave_, int lane) {
+    wave = wave_;
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int slot = (wave + WAVES * i) * 64 + lane;
+      const int r = slot / L::kSlotsPerRow;
+      const int c = slot - r * L::kSlotsPerRow;
+      row[i] = r;
+      col[i] = (c == L::kSlotsPerRow - 1 ? 0 : c) * 8;
+    }
+  }
+  // rows r0 .. r0+ROWS-1 of src (row stride D) into dst
+  __device__ void issue(const bf16* src, int r0, int n, bf16* dst) const {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int b = wave + WAVES * i;
+      if (b < kBlocks) {
+        const int sr = min(r0 + row[i], n - 1);
+        dma16(src + (int64_t)sr * D + col[i], dst + b * 512);
+      }
+    }
+  }
+};
+
 // wait for every outstanding memory operation of this wave
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
