@@ -28,6 +28,26 @@ if ROOT not in sys.path:
 METRIC = "attention fwd/bwd TFLOP/s at n=16384 bf16 on 1 MI355X; % MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0
+COPY_BYTES = 256 << 20
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_bwd_main_n16384_bf16.md")
+KERNEL_SOURCE = os.path.join(ROOT, "memory_efficient_exact_amd", "csrc", "bwd_bf16.hip")
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when the kernel source changed since it was taken."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    h = re.search(r"source sha256: ([0-9a-f]{64})", text)
+    b = re.search(r"HBM bytes per launch: ([0-9.e+]+)", text)
+    if not h or not b or h.group(1) != src:
+        return None
+    return float(b.group(1))
 
 
 def log(*a):
@@ -66,12 +86,72 @@ def cpu_baseline(w):
     }
 
 
+def sweep_configs(steps, warmup):
+    """Per workload: forward (and backward) time, TFLOP/s, peak extra device
+    memory beyond inputs and outputs, and the n^2 fp32 score-matrix size."""
+    import torch
+
+    import inputgen
+    import memory_efficient_exact_amd as mea
+    dev = torch.device("cuda:0")
+    rows = []
+    for name, w in inputgen.WORKLOADS.items():
+        t = inputgen.make_inputs(w, with_do=True)
+        q, k, v, do = (t[x].to(dev) for x in ("q", "k", "v", "do"))
+        o = torch.empty_like(q)
+        m = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        l = torch.empty_like(m)
+        row = {"workload": name, "B": w.B, "H": w.H, "n": w.n, "d": w.d, "dtype": w.dtype,
+               "n2_fp32_score_bytes": 4 * w.B * w.H * w.n * w.n}
+        torch.cuda.synchronize(dev)
+        before = torch.cuda.memory_allocated(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
+
+        def timed(fn):
+            for _ in range(warmup):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize(dev)
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize(dev)
+            return e0.elapsed_time(e1) / steps
+
+        fms = timed(lambda: mea.attn_fwd(q, k, v, out=o, row_max=m, row_sum=l))
+        row["fwd_ms"] = fms
+        row["fwd_tflops"] = w.fwd_flops() / (fms * 1e-3) / 1e12
+        if w.backward:
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+            ws = torch.empty(mea.attn_bwd_workspace_bytes(mea.DTYPE_BF16, w.B, w.H, w.n, w.d),
+                             dtype=torch.uint8, device=dev)
+            before = torch.cuda.memory_allocated(dev)
+            torch.cuda.reset_peak_memory_stats(dev)
+            bms = timed(lambda: mea.attn_bwd(q, k, v, o, do, m, l, dq=dq, dk=dk, dv=dv, workspace=ws))
+            row["bwd_ms"] = bms
+            row["bwd_tflops"] = w.bwd_flops() / (bms * 1e-3) / 1e12
+            row["workspace_bytes"] = ws.numel()
+        row["peak_extra_bytes"] = torch.cuda.max_memory_allocated(dev) - before
+        row["stats_bytes"] = m.numel() * 8
+        rows.append(row)
+        log(json.dumps(row))
+        del t, q, k, v, do, o, m, l
+        torch.cuda.empty_cache()
+    return {"mode": "configs", "steps": steps, "warmup": warmup, "rows": rows}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=("bench", "traffic", "configs"), default="bench",
+                    help="traffic: one 256 MiB copy (counter calibration) and one step, "
+                         "for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs; configs: time "
+                         "the forward on all five workloads (and the backward where the "
+                         "workload trains), one JSON line with a row per workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the attention "
@@ -84,9 +164,12 @@ def main():
     import inputgen
     import memory_efficient_exact_amd as mea
 
-    w = inputgen.WORKLOADS["c3_long_bf16"]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.mode == "configs":
+        print(json.dumps(sweep_configs(args.steps, args.warmup)), flush=True)
+        return
+    w = inputgen.WORKLOADS["c3_long_bf16"]
     t = inputgen.draw(w.B, w.H, w.n, w.d, w.dtype, seed=w.seed, with_do=True)
     q, k, v, do = (t[x].to(dev) for x in ("q", "k", "v", "do"))
     o = torch.empty_like(q)
@@ -97,6 +180,19 @@ def main():
                      dtype=torch.uint8, device=dev)
     io_bytes = sum(x.numel() * x.element_size() for x in (q, k, v, do, o, dq, dk, dv, m, l))
     stream = torch.cuda.current_stream(dev)
+
+    if args.mode == "traffic":
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings give
+        # the factor that turns the counters into bytes.
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        dst.copy_(src)
+        mea.attn_fwd(q, k, v, out=o, row_max=m, row_sum=l, stream=stream)
+        mea.attn_bwd(q, k, v, o, do, m, l, dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream)
+        torch.cuda.synchronize(dev)
+        print(json.dumps({"mode": "traffic", "copy_bytes": COPY_BYTES}), flush=True)
+        return
 
     def step(ev=None):
         if ev is not None:
@@ -147,7 +243,7 @@ def main():
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": bwd_tf / PEAK_BF16_TFLOPS,
-        "traffic": None,
+        "traffic": recorded_traffic(),
         "avg_launch_ms": b_avg,
         "flops_per_launch": bwd_flops,
     }
