@@ -12,7 +12,7 @@
 // dS = P * (dP - D), dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d).
 //
 // Two launches on the caller's stream:
-//  1. bwd_rows: D_i and lse2_i for every row, into the workspace (reads O,
+//  1. bwd_rows: -D_i and lse2_i for every row, into the workspace (reads O,
 //     dO, m, l once; a few microseconds).
 //  2. bwd_main: one grid holding two kinds of workgroup.
 //     * dK/dV workgroups own 128 keys (32 per wave, K and V of those keys in
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (row < rows && part == 0) {
-    Dv[row] = acc;
+    Dv[row] = -acc;  // stored negated: it seeds the dP accumulators below
     Lse2[row] = Mx[row] * kLog2e + __builtin_log2f(Ls[row]);
   }
 }
@@ -76,7 +76,7 @@ struct BwdArgs {
   const bf16* K;
   const bf16* V;
   const bf16* dO;
-  const float* Dv;
+  const float* Dv;    // -D per row
   const float* Lse2;
   bf16* dQ;
   bf16* dK;
@@ -157,18 +157,24 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int wg, bf16* s0, bf
     bf16x8 pf[NC], sf[NC];  // P and dS: chunk c element e <-> query 16c + 8(e/4) + 4hi + e%4
 #pragma unroll
     for (int qb = 0; qb < QBT; ++qb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
+      // lane holds key `key`; register r holds query row i0 + 32*qb + 8*(r/4) + 4*hi + r%4.
+      // The dP accumulator starts at -D of its query row, so it ends at dP - D.
+      f32x16 s = f32x16{}, dp;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 nd = *reinterpret_cast<const f32x4*>(fs + kTileQ + qb * 32 + 8 * r4 + 4 * hi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[4 * r4 + e] = nd[e];
+      }
 #pragma unroll
       for (int dk = 0; dk < DK; ++dk) {
         const int off = a_lane + L::off(qb * 32, dk * 16);
         s = mfma32x32x16(lds_read_b128(qs + off), kf[dk], s);
         dp = mfma32x32x16(lds_read_b128(os + off), vf[dk], dp);
       }
-      // lane holds key `key`; register r holds query row i0 + 32*qb + 8*(r/4) + 4*hi + r%4
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const f32x4 lse = *reinterpret_cast<const f32x4*>(fs + qb * 32 + 8 * r4 + 4 * hi);
-        const f32x4 dd = *reinterpret_cast<const f32x4*>(fs + kTileQ + qb * 32 + 8 * r4 + 4 * hi);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * r4 + e;
@@ -177,7 +183,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int wg, bf16* s0, bf
             if (i0 + qb * 32 + 8 * r4 + 4 * hi + e >= n) p = 0.f;  // padding query rows
           }
           pf[2 * qb + (r >> 3)][r & 7] = (bf16)p;
-          sf[2 * qb + (r >> 3)][r & 7] = (bf16)(p * (dp[r] - dd[e]));
+          sf[2 * qb + (r >> 3)][r & 7] = (bf16)(p * dp[r]);
         }
       }
     }
@@ -261,7 +267,14 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int wg, bf16* s0, bf16
     of[dk] = *reinterpret_cast<const bf16x8*>(a.dO + base + (int64_t)qrow * D + dk * 16 + 8 * hi);
   }
   const float lse = a.Lse2[(int64_t)bh * n + qrow];
-  const float dd = a.Dv[(int64_t)bh * n + qrow];
+  // -D of this query row, in every register: the first dP^T product reads it
+  // as its accumulator input, so dP^T comes out as dP^T - D with no extra VALU.
+  f32x16 ndv;
+  {
+    const float nd = a.Dv[(int64_t)bh * n + qrow];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ndv[r] = nd;
+  }
 
   f32x16 acc[DB];
 #pragma unroll
@@ -278,7 +291,7 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int wg, bf16* s0, bf16
     bf16x8 sf[NC];  // dS^T as B operand, same chunking as P^T in the forward
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
+      f32x16 s = f32x16{}, dp = ndv;
 #pragma unroll
       for (int dk = 0; dk < DK; ++dk) {
         const int off = a_lane + L::off(kb * 32, dk * 16);
@@ -291,7 +304,7 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int wg, bf16* s0, bf16
         if constexpr (kMasked) {
           if (j0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3) >= n) p = 0.f;  // padding keys
         }
-        sf[2 * kb + (r >> 3)][r & 7] = (bf16)(p * (dp[r] - dd));
+        sf[2 * kb + (r >> 3)][r & 7] = (bf16)(p * dp[r]);
       }
     }
     // dQ^T += K^T dS^T (A operand by transposed reads of the K tile)
