@@ -31,6 +31,14 @@ Parity status of each function (what pins it, see tests/test_oracle.py):
 * ``naive_bwd``   - pinned: central finite differences of ``naive_fwd``,
   torch fp64 autograd, exact sum identities, special cases.
 * ``row_stats``   - pinned: brute force (max and sum definitions).
+* ``gqa_fwd`` / ``kv_head_of`` - pinned: per-group constant values fix the
+  head mapping in closed form; brute force per query head; torch fp64 SDPA on
+  explicitly repeated key/value heads.
+* ``gqa_bwd``     - pinned: central finite differences of ``gqa_fwd`` (the
+  shared key/value heads included); torch fp64 autograd.
+* ``block_summary`` / ``merge_summaries`` / ``split_fwd`` - pinned: brute
+  force, ``naive_fwd`` for every split count, order independence of the
+  merge, one-key blocks against the plain definition, 1e4-scale scores.
 """
 
 from .attention import (  # noqa: F401
@@ -40,6 +48,15 @@ from .attention import (  # noqa: F401
     naive_bwd,
     row_stats,
     softmax_scale,
+    kv_head_of,
+    gqa_fwd,
+    gqa_bwd,
+    block_summary,
+    merge_summaries,
+    split_ranges,
+    split_fwd,
 )
 
-__all__ = ["naive_fwd", "chunked_fwd", "single_query", "naive_bwd", "row_stats", "softmax_scale"]
+__all__ = ["naive_fwd", "chunked_fwd", "single_query", "naive_bwd", "row_stats", "softmax_scale",
+           "kv_head_of", "gqa_fwd", "gqa_bwd", "block_summary", "merge_summaries", "split_ranges",
+           "split_fwd"]

@@ -246,3 +246,130 @@ def naive_bwd(q, k, v, do, rows=None, cols=None, row_block=1024):
             dv[g] += p[:, cidx].T @ do3[g, b0:b1]
     return (dq.reshape(lead + dq.shape[1:]), dk.reshape(lead + dk.shape[1:]),
             dv.reshape(lead + dv.shape[1:]))
+
+
+def kv_head_of(h, H, H_kv):
+    """Index of the key/value head that query head ``h`` reads.
+
+    "当注意力成为瓶颈…", section 推理优化：减少KV Cache: grouped-query attention
+    splits the H query heads into H_kv groups and every group shares one
+    key/value head (multi-query attention is the case H_kv = 1). The page does
+    not say which query heads form a group; the reading taken here is
+    consecutive heads: group j holds query heads j*G .. j*G + G - 1, G = H/H_kv.
+    """
+    if H_kv <= 0 or H % H_kv != 0:
+        raise ValueError("H must be a multiple of H_kv")
+    return h // (H // H_kv)
+
+
+def _kv_per_query_head(x, H):
+    """[B, H_kv, n, d] -> [B, H, n, d]: query head h gets key/value head kv_head_of(h)."""
+    x = np.asarray(x, dtype=np.float64)
+    H_kv = x.shape[1]
+    idx = np.array([kv_head_of(h, H, H_kv) for h in range(H)], dtype=np.int64)
+    return x[:, idx]
+
+
+def gqa_fwd(q, k, v, rows=None):
+    """Attention where query head h reads key/value head kv_head_of(h).
+
+    q: [B, H, n_q, d]; k, v: [B, H_kv, n_k, d]. Each query head is plain
+    attention (``naive_fwd``) against the key/value head of its group. Returns
+    (o, m, l) like ``naive_fwd`` with leading axes [B, H].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    H = q.shape[1]
+    return naive_fwd(q, _kv_per_query_head(k, H), _kv_per_query_head(v, H), rows=rows)
+
+
+def gqa_bwd(q, k, v, do, rows=None, cols=None):
+    """Gradients of L = sum(O * dO) for ``gqa_fwd``.
+
+    A key/value head is used by every query head of its group, so by the chain
+    rule its gradient is the sum over that group of the per-query-head
+    gradients of ``naive_bwd`` (same textbook softmax Jacobian). Returns
+    (dq [B, H, ., d], dk [B, H_kv, ., d], dv [B, H_kv, ., d]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, H = q.shape[:2]
+    H_kv = np.asarray(k).shape[1]
+    dq, dk_h, dv_h = naive_bwd(q, _kv_per_query_head(k, H), _kv_per_query_head(v, H), do,
+                               rows=rows, cols=cols)
+    dk = np.zeros((B, H_kv) + dk_h.shape[2:])
+    dv = np.zeros((B, H_kv) + dv_h.shape[2:])
+    for h in range(H):
+        j = kv_head_of(h, H, H_kv)
+        dk[:, j] += dk_h[:, h]
+        dv[:, j] += dv_h[:, h]
+    return dq, dk, dv
+
+
+def block_summary(q, k, v):
+    """Summary of one key/value block for every query row, as the two-block
+    merge of "当注意力成为瓶颈…", section IO感知, uses it: the block's score
+    maximum m_b = max_j s_j, its sum l_b = sum_j exp(s_j - m_b) and its
+    unnormalised output u_b = sum_j exp(s_j - m_b) v_j, s_j = q . k_j / sqrt(d).
+    "Self-attention Does Not Need O(n^2) Memory" (方法详解; English digest
+    method bullets) processes such blocks independently and combines their
+    summaries. q: [..., n, d]; k, v: [..., c, d] with c >= 1.
+    Returns (m [..., n], l [..., n], u [..., n, d]).
+    """
+    q3, lead = _as_slices(q)
+    k3, _ = _as_slices(k)
+    v3, _ = _as_slices(v)
+    if k3.shape[1] == 0:
+        raise ValueError("a block holds at least one key")
+    scale = softmax_scale(q3.shape[2])
+    s = np.einsum("gid,gjd->gij", q3, k3) * scale
+    m = s.max(axis=2)
+    p = np.exp(s - m[:, :, None])
+    l = p.sum(axis=2)
+    u = np.einsum("gij,gjd->gid", p, v3)
+    n = q3.shape[1]
+    return m.reshape(lead + (n,)), l.reshape(lead + (n,)), u.reshape(lead + (n, v3.shape[2]))
+
+
+def merge_summaries(parts):
+    """Combine block summaries (m_b, l_b, u_b) into the exact result.
+
+    The two-block merge of "当注意力成为瓶颈…", section IO感知 (m is the
+    larger block maximum; l and O add the blocks' exponentials re-based on
+    that m), written for any number of blocks at once:
+        m = max_b m_b
+        l = sum_b exp(m_b - m) l_b
+        o = (sum_b exp(m_b - m) u_b) / l
+    Returns (o, m, l).
+    """
+    if not parts:
+        raise ValueError("nothing to merge")
+    m = parts[0][0]
+    for mb, _, _ in parts[1:]:
+        m = np.maximum(m, mb)
+    l = np.zeros_like(parts[0][1])
+    u = np.zeros_like(parts[0][2])
+    for mb, lb, ub in parts:
+        w = np.exp(mb - m)
+        l = l + w * lb
+        u = u + w[..., None] * ub
+    return u / l[..., None], m, l
+
+
+def split_ranges(n_k, splits):
+    """Key ranges [a, b) of ``splits`` near-equal consecutive blocks (each non-empty)."""
+    if n_k <= 0 or splits <= 0:
+        raise ValueError("need n_k >= 1 and splits >= 1")
+    splits = min(splits, n_k)
+    step = -(-n_k // splits)
+    return [(a, min(n_k, a + step)) for a in range(0, n_k, step)]
+
+
+def split_fwd(q, k, v, splits):
+    """Split-key attention: summarise each consecutive key block on its own
+    (``block_summary``) and merge the summaries once (``merge_summaries``).
+    q: [..., n, d]; k, v: [..., n_k, d]. Returns (o, m, l) like ``naive_fwd``.
+    """
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    parts = [block_summary(q, k[..., a:b, :], v[..., a:b, :])
+             for a, b in split_ranges(k.shape[-2], splits)]
+    return merge_summaries(parts)
