@@ -5,6 +5,8 @@ Tolerances (max |gpu - oracle| per element, separately for O, dQ, dK, dV):
   * bf16 inputs: 2e-2, and additionally relative L2 error <= 1e-2 (bf16
     outputs are small, |O| <~ 0.1 at n >= 4096, so 2e-2 alone would admit
     a badly wrong kernel).
+Both bars are absolute for outputs of magnitude <= 1 (every workload) and
+scale with max |reference| beyond that (see ``check``).
 Small shapes are compared in full; the full-size workloads are compared on
 sampled query rows (and sampled key rows for dK/dV), which the oracle
 computes exactly from the complete key set.
@@ -52,12 +54,21 @@ def check(name, got, ref, dtype):
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{name}: non-finite output"
     err = np.abs(got - ref).max() if got.size else 0.0
-    assert err <= TOL[dtype], f"{name}: max abs err {err:.3e} > {TOL[dtype]}"
+    # The bar is absolute for outputs of magnitude <= 1, which holds for every
+    # workload (bf16: |O|, |dQ|, |dK|, |dV| <~ 0.2). Where a test shape has
+    # larger outputs (one key shared by hundreds of query rows sums their dO
+    # into dV), an output in the input type cannot be closer than half its
+    # ulp, so the bar scales with the largest reference value.
+    bar = TOL[dtype] * max(1.0, float(np.abs(ref).max()) if ref.size else 0.0)
+    assert err <= bar, f"{name}: max abs err {err:.3e} > {bar:.3e}"
     if dtype == "bf16" and got.size:
-        # relative L2, with a floor of 1e-4 per element on the denominator so
-        # that an exactly-zero reference (e.g. dQ at n = 1) does not turn
-        # rounding noise into an infinite ratio
-        den = max(np.linalg.norm(ref), 1e-4 * math.sqrt(ref.size))
+        # relative L2, with a floor of 1e-3 rms on the denominator. An exactly
+        # zero reference (dQ at n = 1; dK with a single key, where dP - D
+        # vanishes) leaves only fp32 rounding noise of the order of 1e-6 (the
+        # same dot product summed in two orders); the floor keeps that from
+        # becoming an unbounded ratio. It lies below every output scale of
+        # the workloads (rms |O| >= 0.014 at n = 16384, rms dQ/dK/dV ~ 0.018).
+        den = max(np.linalg.norm(ref), 1e-3 * math.sqrt(ref.size))
         rel = np.linalg.norm(got - ref) / den
         assert rel <= REL_L2_BF16, f"{name}: rel L2 {rel:.3e}"
     return err
