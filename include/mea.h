@@ -15,9 +15,11 @@
  *
  * Conventions shared by every entry point.
  *  - Tensors q, k, v, o, dO, dq, dk, dv are contiguous row-major
- *    [B, H, n, d] arrays in the element type `dt` (d fastest). Self-attention:
- *    queries and keys have the same length n. No mask, no causal structure,
- *    no dropout. The score scale is fixed at 1/sqrt(d).
+ *    [B, H, n, d] arrays in the element type `dt` (d fastest). attn_fwd and
+ *    attn_bwd are self-attention: queries and keys have the same length n
+ *    and every query head has its own key/value head. The *_ex and splitkv
+ *    entry points generalise both (see attn_fwd_ex). No mask, no causal
+ *    structure, no dropout. The score scale is fixed at 1/sqrt(d).
  *  - Every pointer is a DEVICE pointer on the current HIP device, owned by the
  *    caller, and must be 16-byte aligned. The library allocates no device
  *    memory and keeps no state between calls; it is thread-safe.
@@ -31,7 +33,7 @@
  *    hipGetLastError right after the launch; faults during execution surface
  *    at the caller's next synchronisation, as with any HIP kernel.
  *  - Supported: dt in {MEA_DTYPE_BF16, MEA_DTYPE_F32}, d in {64, 128},
- *    1 <= n <= 2^24, B*H <= 2^24.
+ *    n (and n_q, n_k, and (H/H_kv)*n_q) <= 2^24, B*H <= 2^24.
  *  - Accuracy: bf16 inputs are multiplied exactly on bf16 MFMA with fp32
  *    accumulation; probabilities are rounded to bf16 (round-to-nearest-even)
  *    for the P V product; outputs are rounded to bf16 (RNE). fp32 inputs
@@ -46,6 +48,13 @@
 
 #ifdef __cplusplus
 extern "C" {
+#endif
+
+/* Exported symbols of libmea.so (the library is built with hidden visibility). */
+#if defined(__GNUC__) || defined(__clang__)
+#define MEA_API __attribute__((visibility("default")))
+#else
+#define MEA_API
 #endif
 
 typedef enum {
@@ -82,7 +91,7 @@ typedef enum {
  * No workspace: the only memory beyond inputs and outputs is the optional
  * 8*B*H*n bytes of statistics.
  */
-mea_status_t attn_fwd(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d,
+MEA_API mea_status_t attn_fwd(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d,
                       const void* q, const void* k, const void* v, void* o,
                       float* row_max, float* row_sum, void* stream);
 
@@ -91,7 +100,7 @@ mea_status_t attn_fwd(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d
  * 8*B*H*n (two fp32 values per query row: D_i = sum_c dO_ic * O_ic and the
  * base-2 log-sum-exp of the row). Returns 0 for empty or invalid shapes.
  */
-size_t attn_bwd_workspace_bytes(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d);
+MEA_API size_t attn_bwd_workspace_bytes(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d);
 
 /*
  * attn_bwd - backward pass of L = sum(O * dO), by recomputation.
@@ -115,18 +124,103 @@ size_t attn_bwd_workspace_bytes(mea_dtype_t dt, int64_t B, int64_t H, int64_t n,
  * Supported: dt = MEA_DTYPE_BF16 with d in {64, 128}. Other combinations
  * return MEA_ERR_UNSUPPORTED.
  */
-mea_status_t attn_bwd(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d,
+MEA_API mea_status_t attn_bwd(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d,
                       const void* q, const void* k, const void* v, const void* o,
                       const void* dO, const float* row_max, const float* row_sum,
                       void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/*
+ * attn_fwd_ex - forward pass with separate query/key lengths and shared
+ * key/value heads (grouped-query attention; multi-query when H_kv = 1).
+ *
+ * o[b,h,i,:] = sum_j softmax_j(q[b,h,i,:] . k[b,g(h),j,:] / sqrt(d)) v[b,g(h),j,:]
+ * with g(h) = h / (H / H_kv): the H query heads form H_kv groups of
+ * consecutive heads, each reading one key/value head ("当注意力成为瓶颈…",
+ * section 推理优化：减少KV Cache, describes the grouping; taking consecutive
+ * heads is this library's reading). n_q != n_k covers cross-attention and
+ * the decoding step of the same section (a few new queries against a long
+ * key/value cache).
+ *
+ * q, o : [B,H,n_q,d] in dt.   k, v : [B,H_kv,n_k,d] in dt.
+ * row_max, row_sum : fp32 [B,H,n_q] or NULL, as for attn_fwd.
+ * H must be a multiple of H_kv (else MEA_ERR_SHAPE). n_q = 0 is a no-op;
+ * n_k = 0 with n_q > 0 is MEA_ERR_SHAPE (no softmax over zero keys).
+ * attn_fwd(dt,B,H,n,d,...) is attn_fwd_ex(dt,B,H,H,n,n,d,...).
+ */
+MEA_API mea_status_t attn_fwd_ex(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_t n_q,
+                         int64_t n_k, int64_t d, const void* q, const void* k, const void* v,
+                         void* o, float* row_max, float* row_sum, void* stream);
+
+/*
+ * attn_bwd_ex_workspace_bytes - workspace attn_bwd_ex needs: 8*B*H*n_q.
+ * Returns 0 for empty or invalid shapes.
+ */
+MEA_API size_t attn_bwd_ex_workspace_bytes(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv,
+                                   int64_t n_q, int64_t n_k, int64_t d);
+
+/*
+ * attn_bwd_ex - backward pass of attn_fwd_ex (same gradient formulas as
+ * attn_bwd). A key/value head is read by every query head of its group, so
+ * dk and dv are the sums over that group (chain rule).
+ *
+ * q, o, dO, dq : [B,H,n_q,d].   k, v, dk, dv : [B,H_kv,n_k,d].
+ * row_max, row_sum : the [B,H,n_q] statistics attn_fwd_ex wrote.
+ * n_q = 0 with n_k > 0 writes dk = dv = 0 (only k, v, dk, dv are then
+ * checked and the workspace may be NULL); n_k = 0 with n_q > 0 is
+ * MEA_ERR_SHAPE. Supported: dt = MEA_DTYPE_BF16, d in {64, 128}.
+ */
+MEA_API mea_status_t attn_bwd_ex(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_t n_q,
+                         int64_t n_k, int64_t d, const void* q, const void* k, const void* v,
+                         const void* o, const void* dO, const float* row_max,
+                         const float* row_sum, void* dq, void* dk, void* dv, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * attn_fwd_splitkv - attn_fwd_ex with the keys of every head cut into
+ * consecutive ranges that separate workgroups reduce independently, for
+ * grids too small to fill the GPU (few heads, few query rows, decoding).
+ *
+ * "Self-attention Does Not Need O(n^2) Memory" (方法详解; English digest
+ * method bullets) processes key chunks independently and combines their
+ * summaries; "当注意力成为瓶颈…", section IO感知, gives the two-block merge.
+ * Pass 1 writes, per range and query row, the range's normalised partial
+ * output (fp32) and its maximum and sum; pass 2 merges the ranges of every
+ * row and writes o (and row_max / row_sum) exactly as attn_fwd_ex defines
+ * them. The two passes run on `stream` in order.
+ *
+ * num_splits : 0 lets the library choose; k >= 1 asks for k ranges. The
+ *              count used is attn_fwd_splitkv_num_splits(...): at most 256,
+ *              at most one per key tile, every range non-empty. With one
+ *              range this is attn_fwd_ex and needs no workspace.
+ * workspace  : at least attn_fwd_splitkv_workspace_bytes(...) bytes
+ *              (splits * B*H*n_q * (d + 4) * 4), 16-byte aligned, owned by
+ *              the caller; may be NULL when that size is 0. Contents on entry
+ *              do not matter; on return they are unspecified.
+ * Other arguments and errors as attn_fwd_ex; negative num_splits is
+ * MEA_ERR_SHAPE.
+ */
+MEA_API mea_status_t attn_fwd_splitkv(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_t n_q,
+                              int64_t n_k, int64_t d, const void* q, const void* k, const void* v,
+                              void* o, float* row_max, float* row_sum, int64_t num_splits,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* attn_fwd_splitkv_num_splits - number of key ranges attn_fwd_splitkv uses
+ * for these arguments (1 for an empty problem; 0 for invalid arguments). */
+MEA_API int64_t attn_fwd_splitkv_num_splits(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv,
+                                    int64_t n_q, int64_t n_k, int64_t d, int64_t num_splits);
+
+/* attn_fwd_splitkv_workspace_bytes - workspace attn_fwd_splitkv needs for
+ * these arguments (0 when it uses one range, or for empty/invalid shapes). */
+MEA_API size_t attn_fwd_splitkv_workspace_bytes(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv,
+                                        int64_t n_q, int64_t n_k, int64_t d, int64_t num_splits);
+
 /* attn_status_str - static, NUL-terminated name of a status code
  * ("MEA_OK", "MEA_ERR_NULL", ...); "MEA_UNKNOWN_STATUS" for other values. */
-const char* attn_status_str(mea_status_t s);
+MEA_API const char* attn_status_str(mea_status_t s);
 
 /* mea_version - library version as 10000*major + 100*minor + patch. */
-int mea_version(void);
+MEA_API int mea_version(void);
 
 #ifdef __cplusplus
 }

@@ -97,6 +97,33 @@ def draw(B, H, n, d, dtype="bf16", seed=0, qk_scale=1.0, equal_key_heads=(), wit
     return out
 
 
+def draw_gqa(B, H, H_kv, n_q, n_k, d, dtype="bf16", seed=0, qk_scale=1.0, with_do=False):
+    """Like ``draw`` for separate shapes: q (and do) [B, H, n_q, d], k and v
+    [B, H_kv, n_k, d]; same generator, same draw order (q, k, v, do), same
+    rounding. With H_kv = H and n_q = n_k it returns exactly ``draw``'s tensors.
+    """
+    if dtype not in ("fp32", "bf16"):
+        raise ValueError(f"dtype must be 'fp32' or 'bf16', got {dtype!r}")
+    rng = np.random.default_rng(seed)
+    shapes = {"q": (B, H, n_q, d), "k": (B, H_kv, n_k, d), "v": (B, H_kv, n_k, d),
+              "do": (B, H, n_q, d)}
+    raw = {}
+    for nm in ("q", "k", "v", "do"):
+        if nm == "do" and not with_do:
+            break
+        raw[nm] = rng.standard_normal(shapes[nm], dtype=np.float64)
+    if qk_scale != 1.0:
+        raw["q"] = raw["q"] * qk_scale
+        raw["k"] = raw["k"] * qk_scale
+    out = {}
+    for nm, a in raw.items():
+        t = torch.from_numpy(np.ascontiguousarray(a.astype(np.float32)))
+        if dtype == "bf16":
+            t = t.to(torch.bfloat16)
+        out[nm] = t.contiguous()
+    return out
+
+
 def make_inputs(w: Workload, seed=None, with_do=None):
     """Inputs for workload ``w`` (seed defaults to the workload's own)."""
     return draw(w.B, w.H, w.n, w.d, w.dtype, w.seed if seed is None else seed,

@@ -14,6 +14,8 @@ import os
 __all__ = [
     "MeaError", "DTYPE_F32", "DTYPE_BF16", "lib", "library_path",
     "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str", "mea_version",
+    "attn_fwd_ex", "attn_bwd_ex", "attn_bwd_ex_workspace_bytes",
+    "attn_fwd_splitkv", "attn_fwd_splitkv_num_splits", "attn_fwd_splitkv_workspace_bytes",
 ]
 
 DTYPE_F32 = 0
@@ -56,6 +58,19 @@ def lib():
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_bwd.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_bwd.restype = i32
+    L.attn_fwd_ex.argtypes = [i32, i64, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+    L.attn_fwd_ex.restype = i32
+    L.attn_bwd_ex_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i64, i64]
+    L.attn_bwd_ex_workspace_bytes.restype = sz
+    L.attn_bwd_ex.argtypes = [i32, i64, i64, i64, i64, i64, i64] + [vp] * 11 + [sz, vp]
+    L.attn_bwd_ex.restype = i32
+    L.attn_fwd_splitkv.argtypes = [i32, i64, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, i64,
+                                   vp, sz, vp]
+    L.attn_fwd_splitkv.restype = i32
+    L.attn_fwd_splitkv_num_splits.argtypes = [i32, i64, i64, i64, i64, i64, i64, i64]
+    L.attn_fwd_splitkv_num_splits.restype = i64
+    L.attn_fwd_splitkv_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i64, i64, i64]
+    L.attn_fwd_splitkv_workspace_bytes.restype = sz
     L.attn_status_str.argtypes = [i32]
     L.attn_status_str.restype = ctypes.c_char_p
     L.mea_version.argtypes = []
@@ -79,6 +94,20 @@ def mea_version():
 
 def attn_bwd_workspace_bytes(dt, B, H, n, d):
     return lib().attn_bwd_workspace_bytes(int(dt), int(B), int(H), int(n), int(d))
+
+
+def attn_bwd_ex_workspace_bytes(dt, B, H, H_kv, n_q, n_k, d):
+    return lib().attn_bwd_ex_workspace_bytes(*(int(x) for x in (dt, B, H, H_kv, n_q, n_k, d)))
+
+
+def attn_fwd_splitkv_num_splits(dt, B, H, H_kv, n_q, n_k, d, num_splits=0):
+    return lib().attn_fwd_splitkv_num_splits(
+        *(int(x) for x in (dt, B, H, H_kv, n_q, n_k, d, num_splits)))
+
+
+def attn_fwd_splitkv_workspace_bytes(dt, B, H, H_kv, n_q, n_k, d, num_splits=0):
+    return lib().attn_fwd_splitkv_workspace_bytes(
+        *(int(x) for x in (dt, B, H, H_kv, n_q, n_k, d, num_splits)))
 
 
 # ------------------------------------------------------------ torch marshalling
@@ -112,6 +141,54 @@ def _check_stat(name, t, q):
     import torch
     if t.dtype != torch.float32 or not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous float32")
+
+
+def _check_as(name, t, shape, like):
+    """t must be a contiguous GPU tensor of `shape` with like's dtype and device."""
+    if not t.is_cuda or t.device != like.device:
+        raise ValueError(f"{name} must be a GPU tensor on {like.device}")
+    if tuple(t.shape) != tuple(shape) or t.dtype != like.dtype:
+        raise ValueError(f"{name} must have shape {tuple(shape)} dtype {like.dtype}, "
+                         f"got {tuple(t.shape)} {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _gqa_shapes(q, k, v):
+    """(B, H, H_kv, n_q, n_k, d) of q [B,H,n_q,d] and k, v [B,H_kv,n_k,d]."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, n_q, d] and k, v [B, H_kv, n_k, d]")
+    B, H, n_q, d = q.shape
+    H_kv, n_k = k.shape[1], k.shape[2]
+    _check_as("q", q, q.shape, q)
+    _check_as("k", k, (B, H_kv, n_k, d), q)
+    _check_as("v", v, (B, H_kv, n_k, d), q)
+    return B, H, H_kv, n_q, n_k, d
+
+
+def _fwd_outputs(q, out, row_max, row_sum, stats):
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    _check_as("out", out, q.shape, q)
+    if (row_max is None) != (row_sum is None):
+        raise ValueError("pass both row_max and row_sum, or neither")
+    if row_max is None and stats:
+        row_max = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+        row_sum = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if row_max is not None:
+        _check_stat("row_max", row_max, q)
+        _check_stat("row_sum", row_sum, q)
+    return out, row_max, row_sum
+
+
+def _workspace(workspace, need, device):
+    import torch
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return workspace, workspace.numel() * workspace.element_size()
 
 
 def _stream(stream, device):
@@ -192,3 +269,68 @@ def attn_bwd(q, k, v, o, do, row_max, row_sum, dq=None, dk=None, dv=None, worksp
     if st != 0:
         raise MeaError("attn_bwd", st)
     return dq, dk, dv
+
+
+def attn_fwd_ex(q, k, v, out=None, row_max=None, row_sum=None, stats=True, stream=None):
+    """Forward with separate lengths and shared key/value heads: q [B, H, n_q, d],
+    k and v [B, H_kv, n_k, d] with H a multiple of H_kv; query head h reads
+    key/value head h // (H // H_kv). Returns (o, row_max, row_sum) as ``attn_fwd``."""
+    import torch
+    dt = _dtype_code(q)
+    B, H, H_kv, n_q, n_k, d = _gqa_shapes(q, k, v)
+    out, row_max, row_sum = _fwd_outputs(q, out, row_max, row_sum, stats)
+    with torch.cuda.device(q.device):
+        st = lib().attn_fwd_ex(dt, B, H, H_kv, n_q, n_k, d, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                               _ptr(row_max), _ptr(row_sum), _stream(stream, q.device))
+    if st != 0:
+        raise MeaError("attn_fwd_ex", st)
+    return out, row_max, row_sum
+
+
+def attn_bwd_ex(q, k, v, o, do, row_max, row_sum, dq=None, dk=None, dv=None, workspace=None,
+                stream=None):
+    """Backward of ``attn_fwd_ex``: (dq [B, H, n_q, d], dk and dv [B, H_kv, n_k, d]);
+    dk and dv sum over the query heads that share each key/value head."""
+    import torch
+    dt = _dtype_code(q)
+    B, H, H_kv, n_q, n_k, d = _gqa_shapes(q, k, v)
+    _check_as("o", o, q.shape, q)
+    _check_as("do", do, q.shape, q)
+    _check_stat("row_max", row_max, q)
+    _check_stat("row_sum", row_sum, q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_as("dq", dq, q.shape, q)
+    _check_as("dk", dk, k.shape, q)
+    _check_as("dv", dv, v.shape, q)
+    workspace, wbytes = _workspace(workspace, attn_bwd_ex_workspace_bytes(dt, B, H, H_kv, n_q, n_k, d),
+                                   q.device)
+    with torch.cuda.device(q.device):
+        st = lib().attn_bwd_ex(dt, B, H, H_kv, n_q, n_k, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                               _ptr(do), _ptr(row_max), _ptr(row_sum), _ptr(dq), _ptr(dk),
+                               _ptr(dv), _ptr(workspace), wbytes, _stream(stream, q.device))
+    if st != 0:
+        raise MeaError("attn_bwd_ex", st)
+    return dq, dk, dv
+
+
+def attn_fwd_splitkv(q, k, v, num_splits=0, out=None, row_max=None, row_sum=None, stats=True,
+                     workspace=None, stream=None):
+    """``attn_fwd_ex`` with every head's keys cut into ranges reduced by separate
+    workgroups and merged afterwards (for small grids and decoding).
+    ``num_splits`` 0 lets the library choose. ``workspace`` (a GPU tensor of at
+    least ``attn_fwd_splitkv_workspace_bytes`` bytes) is allocated if not passed."""
+    import torch
+    dt = _dtype_code(q)
+    B, H, H_kv, n_q, n_k, d = _gqa_shapes(q, k, v)
+    out, row_max, row_sum = _fwd_outputs(q, out, row_max, row_sum, stats)
+    need = attn_fwd_splitkv_workspace_bytes(dt, B, H, H_kv, n_q, n_k, d, num_splits)
+    workspace, wbytes = _workspace(workspace, need, q.device)
+    with torch.cuda.device(q.device):
+        st = lib().attn_fwd_splitkv(dt, B, H, H_kv, n_q, n_k, d, _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(out), _ptr(row_max), _ptr(row_sum), int(num_splits),
+                                    _ptr(workspace), wbytes, _stream(stream, q.device))
+    if st != 0:
+        raise MeaError("attn_fwd_splitkv", st)
+    return out, row_max, row_sum

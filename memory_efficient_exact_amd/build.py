@@ -25,6 +25,8 @@ FLAGS = [
     # explicitly, and the softmax bookkeeping relies on rounded products
     # (fl(m*C)) staying rounded
     "-ffp-contract=off",
+    # only the C ABI (marked MEA_API in include/mea.h) is exported
+    "-fvisibility=hidden",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

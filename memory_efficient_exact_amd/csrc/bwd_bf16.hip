@@ -28,6 +28,11 @@
 //     dQ workgroups fill the machine behind them.
 // No probability or score array is written to memory; dQ, dK and dV are each
 // written once by one workgroup, so results do not depend on scheduling.
+//
+// Grouped-query heads: the query heads sharing one key/value head arrive
+// stacked as the rows of one problem (see mea_launch.h), so a dK/dV workgroup
+// sweeps the query rows of the whole group and its dK, dV are the sums over
+// that group that the chain rule asks for, still written once.
 #include <type_traits>
 
 #include "mea_device.h"
@@ -81,9 +86,10 @@ struct BwdArgs {
   bf16* dQ;
   bf16* dK;
   bf16* dV;
-  int n;
-  int tiles_kv;   // dK/dV workgroups per (b, h)
-  int tiles_q;    // dQ workgroups per (b, h)
+  int n_q;        // query rows per head (the query heads of a group, stacked)
+  int n_k;        // keys per head
+  int tiles_kv;   // dK/dV workgroups per head
+  int tiles_q;    // dQ workgroups per head
   int total_kv;   // dK/dV workgroups in the grid
   int total_q;    // dQ workgroups in the grid
   float C;        // log2(e) / sqrt(d)
@@ -110,23 +116,24 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int wg, bf16* s0, bf
   constexpr int NC = kTileQ / 16;  // 16-query chunks per tile
   constexpr int QBT = kTileQ / 32; // 32-query blocks per tile
 
-  const int n = a.n;
+  const int n_q = a.n_q, n_k = a.n_k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int tile = xcd_remap(wg, a.total_kv);
   const int bh = tile / a.tiles_kv;
   const int kt = tile - bh * a.tiles_kv;
-  const int64_t base = (int64_t)bh * n * D;
-  const int64_t rbase = (int64_t)bh * n;
+  const int64_t qbase = (int64_t)bh * n_q * D;  // Q, dO (all query rows of the head)
+  const int64_t kbase = (int64_t)bh * n_k * D;  // K, V, dK, dV
+  const int64_t rbase = (int64_t)bh * n_q;
   const int key = kt * kRowsKV + wave * 32 + l32;  // this lane's key (column of S)
 
   // K and V of this wave's 32 keys: B operands of S = Q K^T and dP = dO V^T
   bf16x8 kf[DK], vf[DK];
-  const int krow = min(key, n - 1);
+  const int krow = min(key, n_k - 1);
 #pragma unroll
   for (int dk = 0; dk < DK; ++dk) {
-    kf[dk] = *reinterpret_cast<const bf16x8*>(a.K + base + (int64_t)krow * D + dk * 16 + 8 * hi);
-    vf[dk] = *reinterpret_cast<const bf16x8*>(a.V + base + (int64_t)krow * D + dk * 16 + 8 * hi);
+    kf[dk] = *reinterpret_cast<const bf16x8*>(a.K + kbase + (int64_t)krow * D + dk * 16 + 8 * hi);
+    vf[dk] = *reinterpret_cast<const bf16x8*>(a.V + kbase + (int64_t)krow * D + dk * 16 + 8 * hi);
   }
   f32x16 accV[DB], accK[DB];  // dV^T, dK^T: register r -> column 32*db + 8*(r/4) + 4*hi + r%4
 #pragma unroll
@@ -139,10 +146,10 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int wg, bf16* s0, bf
   dma.init(wave, lane);
   // lse2 and D of a query tile: 64 floats each, one 4-byte DMA per lane
   auto issue = [&](bf16* qdst, bf16* odst, float* fdst, int i0) {
-    dma.issue(a.Q + base, i0, n, qdst);
-    dma.issue(a.dO + base, i0, n, odst);
+    dma.issue(a.Q + qbase, i0, n_q, qdst);
+    dma.issue(a.dO + qbase, i0, n_q, odst);
     if (wave == kWaves - 1) {
-      const int r = min(i0 + lane, n - 1);
+      const int r = min(i0 + lane, n_q - 1);
       dma4(a.Lse2 + rbase + r, fdst);
       dma4(a.Dv + rbase + r, fdst + kTileQ);
     }
@@ -180,7 +187,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int wg, bf16* s0, bf
           const int r = 4 * r4 + e;
           float p = fast_exp2(__builtin_fmaf(s[r], a.C, -lse[e]));
           if constexpr (kMasked) {
-            if (i0 + qb * 32 + 8 * r4 + 4 * hi + e >= n) p = 0.f;  // padding query rows
+            if (i0 + qb * 32 + 8 * r4 + 4 * hi + e >= n_q) p = 0.f;  // padding query rows
           }
           pf[2 * qb + (r >> 3)][r & 7] = (bf16)p;
           sf[2 * qb + (r >> 3)][r & 7] = (bf16)(p * dp[r]);
@@ -201,27 +208,29 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int wg, bf16* s0, bf
     }
   };
 
-  const int ntiles = (n + kTileQ - 1) / kTileQ;
+  const int ntiles = (n_q + kTileQ - 1) / kTileQ;
   auto step = [&](const bf16* qs, const bf16* os, const float* fs, bf16* qn, bf16* on, float* fn,
                   int t) {
     const int i0 = t * kTileQ;
     if (t + 1 < ntiles) issue(qn, on, fn, i0 + kTileQ);
-    if (i0 + kTileQ <= n) tile_body(qs, os, fs, i0, std::false_type{});
+    if (i0 + kTileQ <= n_q) tile_body(qs, os, fs, i0, std::false_type{});
     else tile_body(qs, os, fs, i0, std::true_type{});
     wait_all();
     __syncthreads();
   };
-  issue(s0, s1, f0, 0);
-  wait_all();
-  __syncthreads();
+  if (ntiles > 0) {  // no query rows at all: dK = dV = 0
+    issue(s0, s1, f0, 0);
+    wait_all();
+    __syncthreads();
+  }
   for (int t = 0; t < ntiles; t += 2) {
     step(s0, s1, f0, s2, s3, f1, t);
     if (t + 1 < ntiles) step(s2, s3, f1, s0, s1, f0, t + 1);
   }
 
-  if (key < n) {
-    bf16* vrow = a.dV + base + (int64_t)key * D;
-    bf16* krow_out = a.dK + base + (int64_t)key * D;
+  if (key < n_k) {
+    bf16* vrow = a.dV + kbase + (int64_t)key * D;
+    bf16* krow_out = a.dK + kbase + (int64_t)key * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -250,28 +259,29 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int wg, bf16* s0, bf16
   constexpr int KB = kTileK / 32;
   constexpr int NC = kTileK / 16;
 
-  const int n = a.n;
+  const int n_q = a.n_q, n_k = a.n_k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int tile = xcd_remap(wg, a.total_q);
   const int bh = tile / a.tiles_q;
   const int qt = tile - bh * a.tiles_q;
-  const int64_t base = (int64_t)bh * n * D;
+  const int64_t qbase = (int64_t)bh * n_q * D;  // Q, dO, dQ
+  const int64_t kbase = (int64_t)bh * n_k * D;  // K, V
   const int row = qt * kRowsQ + wave * 32 + l32;  // this lane's query
-  const int qrow = min(row, n - 1);
+  const int qrow = min(row, n_q - 1);
 
   bf16x8 qf[DK], of[DK];  // B operands of S^T = K Q^T and dP^T = V dO^T
 #pragma unroll
   for (int dk = 0; dk < DK; ++dk) {
-    qf[dk] = *reinterpret_cast<const bf16x8*>(a.Q + base + (int64_t)qrow * D + dk * 16 + 8 * hi);
-    of[dk] = *reinterpret_cast<const bf16x8*>(a.dO + base + (int64_t)qrow * D + dk * 16 + 8 * hi);
+    qf[dk] = *reinterpret_cast<const bf16x8*>(a.Q + qbase + (int64_t)qrow * D + dk * 16 + 8 * hi);
+    of[dk] = *reinterpret_cast<const bf16x8*>(a.dO + qbase + (int64_t)qrow * D + dk * 16 + 8 * hi);
   }
-  const float lse = a.Lse2[(int64_t)bh * n + qrow];
+  const float lse = a.Lse2[(int64_t)bh * n_q + qrow];
   // -D of this query row, in every register: the first dP^T product reads it
   // as its accumulator input, so dP^T comes out as dP^T - D with no extra VALU.
   f32x16 ndv;
   {
-    const float nd = a.Dv[(int64_t)bh * n + qrow];
+    const float nd = a.Dv[(int64_t)bh * n_q + qrow];
 #pragma unroll
     for (int r = 0; r < 16; ++r) ndv[r] = nd;
   }
@@ -302,7 +312,7 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int wg, bf16* s0, bf16
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(__builtin_fmaf(s[r], a.C, -lse));
         if constexpr (kMasked) {
-          if (j0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3) >= n) p = 0.f;  // padding keys
+          if (j0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3) >= n_k) p = 0.f;  // padding keys
         }
         sf[2 * kb + (r >> 3)][r & 7] = (bf16)(p * dp[r]);
       }
@@ -319,20 +329,20 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int wg, bf16* s0, bf16
     }
   };
 
-  const int ntiles = (n + kTileK - 1) / kTileK;
+  const int ntiles = (n_k + kTileK - 1) / kTileK;
   auto step = [&](const bf16* ks, const bf16* vs, bf16* kn, bf16* vn, int t) {
     const int j0 = t * kTileK;
     if (t + 1 < ntiles) {
-      dma.issue(a.K + base, j0 + kTileK, n, kn);
-      dma.issue(a.V + base, j0 + kTileK, n, vn);
+      dma.issue(a.K + kbase, j0 + kTileK, n_k, kn);
+      dma.issue(a.V + kbase, j0 + kTileK, n_k, vn);
     }
-    if (j0 + kTileK <= n) tile_body(ks, vs, j0, std::false_type{});
+    if (j0 + kTileK <= n_k) tile_body(ks, vs, j0, std::false_type{});
     else tile_body(ks, vs, j0, std::true_type{});
     wait_all();
     __syncthreads();
   };
-  dma.issue(a.K + base, 0, n, s0);
-  dma.issue(a.V + base, 0, n, s1);
+  dma.issue(a.K + kbase, 0, n_k, s0);
+  dma.issue(a.V + kbase, 0, n_k, s1);
   wait_all();
   __syncthreads();
   for (int t = 0; t < ntiles; t += 2) {
@@ -340,8 +350,8 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int wg, bf16* s0, bf16
     if (t + 1 < ntiles) step(s2, s3, s0, s1, t + 1);
   }
 
-  if (row < n) {
-    bf16* qout = a.dQ + base + (int64_t)row * D;
+  if (row < n_q) {
+    bf16* qout = a.dQ + qbase + (int64_t)row * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -371,35 +381,34 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void bwd_main_kernel(Bwd
 }
 
 template <int D>
-hipError_t launch(int64_t BH, int n, const void* q, const void* k, const void* v, const void* o,
-                  const void* dO, const float* m, const float* l, void* dq, void* dk, void* dv,
-                  float* ws, hipStream_t stream) {
-  const int64_t rows = BH * n;
-  float* Dv = ws;
-  float* Lse2 = ws + rows;
-  {
+hipError_t launch(const BwdProblem& p, hipStream_t stream) {
+  const int64_t rows = p.heads * p.rows_q;
+  float* Dv = p.ws;
+  float* Lse2 = p.ws + rows;
+  if (rows > 0) {
     const int64_t threads = rows * (D / 8);
     const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
     hipLaunchKernelGGL((bwd_rows_kernel<D>), dim3(blocks), dim3(kThreads), 0, stream,
-                       (const bf16*)o, (const bf16*)dO, m, l, Dv, Lse2, rows);
+                       (const bf16*)p.o, (const bf16*)p.dO, p.m, p.l, Dv, Lse2, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   BwdArgs a;
-  a.Q = (const bf16*)q;
-  a.K = (const bf16*)k;
-  a.V = (const bf16*)v;
-  a.dO = (const bf16*)dO;
+  a.Q = (const bf16*)p.q;
+  a.K = (const bf16*)p.k;
+  a.V = (const bf16*)p.v;
+  a.dO = (const bf16*)p.dO;
   a.Dv = Dv;
   a.Lse2 = Lse2;
-  a.dQ = (bf16*)dq;
-  a.dK = (bf16*)dk;
-  a.dV = (bf16*)dv;
-  a.n = n;
-  a.tiles_kv = (n + kRowsKV - 1) / kRowsKV;
-  a.tiles_q = (n + kRowsQ - 1) / kRowsQ;
-  a.total_kv = (int)(BH * a.tiles_kv);
-  a.total_q = (int)(BH * a.tiles_q);
+  a.dQ = (bf16*)p.dq;
+  a.dK = (bf16*)p.dk;
+  a.dV = (bf16*)p.dv;
+  a.n_q = p.rows_q;
+  a.n_k = p.n_k;
+  a.tiles_kv = (p.n_k + kRowsKV - 1) / kRowsKV;
+  a.tiles_q = (p.rows_q + kRowsQ - 1) / kRowsQ;
+  a.total_kv = (int)(p.heads * a.tiles_kv);
+  a.total_q = (int)(p.heads * a.tiles_q);
   a.scale = 1.0f / sqrtf((float)D);
   a.C = kLog2e * a.scale;
   hipLaunchKernelGGL((bwd_main_kernel<D>), dim3((unsigned)(a.total_kv + a.total_q)), dim3(kThreads),
@@ -409,11 +418,9 @@ hipError_t launch(int64_t BH, int n, const void* q, const void* k, const void* v
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(int d, int64_t BH, int n, const void* q, const void* k, const void* v,
-                           const void* o, const void* dO, const float* m, const float* l,
-                           void* dq, void* dk, void* dv, float* ws, hipStream_t stream) {
-  if (d == 64) return launch<64>(BH, n, q, k, v, o, dO, m, l, dq, dk, dv, ws, stream);
-  return launch<128>(BH, n, q, k, v, o, dO, m, l, dq, dk, dv, ws, stream);
+hipError_t launch_bwd_bf16(int d, const BwdProblem& p, hipStream_t stream) {
+  if (d == 64) return launch<64>(p, stream);
+  return launch<128>(p, stream);
 }
 
 }  // namespace mea

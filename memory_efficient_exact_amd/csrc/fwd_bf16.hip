@@ -31,6 +31,13 @@
 // before, and the O(d) rescale of the accumulators is skipped for almost every
 // block. The true running max m is tracked separately; the statistics are
 // reported for it: l = sum_j exp(s_j - m) = l_R * exp2(R - m*C).
+//
+// Key ranges. A workgroup may cover only the keys [key0, key0 + split_len) of its
+// head (split-key mode, for grids too small to fill the chip). It then writes
+// the summary of that range instead of the output: the normalised fp32 row
+// acc / l_R, the exact raw maximum m, the reference R and l_R. The merge pass
+// (merge.hip) combines the ranges of a row with the two-block merge of
+// "当注意力成为瓶颈…", section IO感知.
 #include <type_traits>
 
 #include "mea_device.h"
@@ -43,11 +50,28 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kRefSlack = 8.0f;  // log2 units a row max may exceed its reference
 
+struct FwdArgs {
+  const bf16* Q;  // [heads, n_q, D]
+  const bf16* K;  // [heads, n_k, D]
+  const bf16* V;
+  bf16* O;        // final mode: [heads, n_q, D]
+  float* Mx;      // final mode: [heads, n_q] or null
+  float* Ls;
+  float* Po;      // split mode: [splits, rows, D] normalised partial rows (else null)
+  float* Ps;      // split mode: [splits, rows] records {m, R, l_R, 0}
+  int64_t rows;   // heads * n_q
+  int n_q;
+  int n_k;
+  int qtiles;     // query tiles per head
+  int splits;     // key ranges per head
+  int split_len;  // keys per range (n_k when splits == 1)
+  int total;      // workgroups
+  float C;        // log2(e) / sqrt(D)
+  float scale;    // 1 / sqrt(D)
+};
+
 template <int D, int QB, int BC>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ Mx, float* __restrict__ Ls,
-    int n, int qtiles, int total, float C, float scale) {
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const FwdArgs a) {
   constexpr int kBQ = kWaves * QB * 32;  // query rows per workgroup
   constexpr int DK = D / 16;             // k-steps of the score MFMA
   constexpr int DB = D / 32;             // 32-wide output column blocks
@@ -74,13 +98,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const int tile = xcd_remap(blockIdx.x, total);
-  const int bh = tile / qtiles;
-  const int qt = tile - bh * qtiles;
-  const int64_t base = (int64_t)bh * n * D;
-  const bf16* Qh = Q + base;
-  const bf16* Kh = K + base;
-  const bf16* Vh = V + base;
+  // workgroup -> (head, key range, query tile); the query tiles of one key
+  // range are adjacent, so they share an XCD and its L2 copy of K and V
+  const int tile = xcd_remap(blockIdx.x, a.total);
+  const int hs = tile / a.qtiles;
+  const int qt = tile - hs * a.qtiles;
+  const int bh = hs / a.splits;
+  const int sp = hs - bh * a.splits;
+  const int key0 = sp * a.split_len;            // first key of this range
+  const int n = min(a.n_k - key0, a.split_len);  // keys of this range
+  const int n_q = a.n_q;
+  const float C = a.C;
+  const bf16* Qh = a.Q + (int64_t)bh * n_q * D;
+  const bf16* Kh = a.K + ((int64_t)bh * a.n_k + key0) * D;
+  const bf16* Vh = a.V + ((int64_t)bh * a.n_k + key0) * D;
   const int q0 = qt * kBQ + wave * QB * 32;
 
   // Q fragments: B operand of S^T = K Q^T (lane: query l32, 8 columns at 16*dk + 8*hi)
@@ -90,8 +121,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const int row = q0 + qb * 32 + l32;
 #pragma unroll
     for (int dk = 0; dk < DK; ++dk) {
-      qf[qb][dk] = row < n ? *reinterpret_cast<const bf16x8*>(Qh + (int64_t)row * D + dk * 16 + 8 * hi)
-                           : bf16x8{};
+      qf[qb][dk] = row < n_q ? *reinterpret_cast<const bf16x8*>(Qh + (int64_t)row * D + dk * 16 + 8 * hi)
+                             : bf16x8{};
     }
   }
 
@@ -234,8 +265,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     const int row = q0 + qb * 32 + l32;
     const float l_tot = pair_sum32(l_run[qb]);
     const float inv = 1.f / l_tot;
-    if (row < n) {
-      bf16* orow = O + base + (int64_t)row * D;
+    if (row >= n_q) continue;
+    const int64_t grow = (int64_t)bh * n_q + row;
+    if (a.Po == nullptr) {
+      bf16* orow = a.O + grow * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -245,37 +278,69 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
           for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[qb][db][4 * r4 + e] * inv);
           *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * r4 + 4 * hi) = w;
         }
-      if (Mx != nullptr && hi == 0) {
+      if (a.Mx != nullptr && hi == 0) {
         // l_tot sums exp2(x*C - R) = exp(s - m) * 2^(m*C - R); m*C - R is
         // formed exactly by one FMA
         const float shift = __builtin_fmaf(m_run[qb], C, -ref[qb]);
-        Mx[(int64_t)bh * n + row] = m_run[qb] * scale;
-        Ls[(int64_t)bh * n + row] = l_tot * fast_exp2(-shift);
+        a.Mx[grow] = m_run[qb] * a.scale;
+        a.Ls[grow] = l_tot * fast_exp2(-shift);
       }
+    } else {
+      // summary of this key range: acc / l_R in fp32 and {m, R, l_R}
+      const int64_t prow = (int64_t)sp * a.rows + grow;
+      float* orow = a.Po + prow * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = acc[qb][db][4 * r4 + e] * inv;
+          *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * r4 + 4 * hi) = w;
+        }
+      if (hi == 0) *reinterpret_cast<f32x4*>(a.Ps + prow * 4) = f32x4{m_run[qb], ref[qb], l_tot, 0.f};
     }
   }
 }
 
 template <int D, int QB, int BC>
-hipError_t launch(int64_t BH, int n, const void* q, const void* k, const void* v, void* o,
-                  float* m, float* l, hipStream_t stream) {
+hipError_t launch(const FwdProblem& p, hipStream_t stream) {
   constexpr int kBQ = kWaves * QB * 32;
-  const int qtiles = (n + kBQ - 1) / kBQ;
-  const int64_t total = BH * qtiles;
-  const float scale = 1.0f / sqrtf((float)D);
-  const float C = kLog2e * scale;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BC>), dim3((unsigned)total), dim3(kThreads), 0, stream,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, m, l, n, qtiles,
-                     (int)total, C, scale);
+  FwdArgs a;
+  a.Q = static_cast<const bf16*>(p.q);
+  a.K = static_cast<const bf16*>(p.k);
+  a.V = static_cast<const bf16*>(p.v);
+  a.O = static_cast<bf16*>(p.o);
+  a.Mx = p.m;
+  a.Ls = p.l;
+  a.rows = p.heads * p.rows_q;
+  a.n_q = p.rows_q;
+  a.n_k = p.n_k;
+  a.qtiles = (p.rows_q + kBQ - 1) / kBQ;
+  a.splits = p.splits > 1 ? p.splits : 1;
+  a.split_len = p.splits > 1 ? p.split_len : p.n_k;
+  a.Po = p.splits > 1 ? p.part : nullptr;
+  a.Ps = p.splits > 1 ? p.part + (int64_t)a.splits * a.rows * D : nullptr;
+  const int64_t total = p.heads * a.splits * a.qtiles;
+  a.total = (int)total;
+  a.scale = 1.0f / sqrtf((float)D);
+  a.C = kLog2e * a.scale;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BC>), dim3((unsigned)total), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
+// d = 64: 256 query rows and 128-key tiles per workgroup; d = 128: 128 rows, 64 keys
+constexpr int kQB64 = 2, kBC64 = 128, kQB128 = 1, kBC128 = 64;
+
 }  // namespace
 
-hipError_t launch_fwd_bf16(int d, int64_t BH, int n, const void* q, const void* k, const void* v,
-                           void* o, float* m, float* l, hipStream_t stream) {
-  if (d == 64) return launch<64, 2, 128>(BH, n, q, k, v, o, m, l, stream);
-  return launch<128, 1, 64>(BH, n, q, k, v, o, m, l, stream);
+FwdGeometry fwd_geometry_bf16(int d) {
+  return d == 64 ? FwdGeometry{kWaves * kQB64 * 32, kBC64} : FwdGeometry{kWaves * kQB128 * 32, kBC128};
+}
+
+hipError_t launch_fwd_bf16(int d, const FwdProblem& p, hipStream_t stream) {
+  if (d == 64) return launch<64, kQB64, kBC64>(p, stream);
+  return launch<128, kQB128, kBC128>(p, stream);
 }
 
 }  // namespace mea

@@ -14,6 +14,11 @@
 // double-buffered, rows padded so the column reads of both MFMA operands hit
 // distinct banks. The score tile is transposed (lane = query), so the per-row
 // state lives in registers; four lanes (l, l^16, l^32, l^48) share a query.
+//
+// Key ranges (split-key mode): a workgroup may cover only keys
+// [key0, key0 + split_len) of its head and then writes that range's summary, the
+// fp32 row acc / l, the fp64 maximum m and l (relative to m), for the merge
+// pass (merge.hip).
 #include "mea_device.h"
 #include "mea_launch.h"
 
@@ -29,11 +34,28 @@ __device__ __forceinline__ float xor16f(float x) { return __shfl_xor(x, 16, 64);
 __device__ __forceinline__ double xor16d(double x) { return __shfl_xor(x, 16, 64); }
 __device__ __forceinline__ double xor32d(double x) { return __shfl_xor(x, 32, 64); }
 
+struct FwdArgs32 {
+  const float* Q;  // [heads, n_q, D]
+  const float* K;  // [heads, n_k, D]
+  const float* V;
+  float* O;        // final mode: [heads, n_q, D]
+  float* Mx;       // final mode: [heads, n_q] or null
+  float* Ls;
+  float* Po;       // split mode: [splits, rows, D] normalised partial rows (else null)
+  float* Ps;       // split mode: [splits, rows] records {m (fp64, two words), l, 0}
+  int64_t rows;    // heads * n_q
+  int n_q;
+  int n_k;
+  int qtiles;
+  int splits;
+  int split_len;
+  int total;
+  double C64;      // log2(e) / sqrt(D)
+  double scale64;  // 1 / sqrt(D)
+};
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
-    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ Mx, float* __restrict__ Ls,
-    int n, int qtiles, int total, double C64, double scale64) {
+__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs32 a) {
   constexpr int KS = D + 4;   // K row stride (floats): 16-byte pad
   constexpr int VS = D + 16;  // V row stride (floats): 64-byte pad
   constexpr int KK = D / 4;   // k-steps of the fp64 score MFMA
@@ -52,19 +74,26 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
 
-  const int tile = xcd_remap(blockIdx.x, total);
-  const int bh = tile / qtiles;
-  const int qt = tile - bh * qtiles;
-  const int64_t base = (int64_t)bh * n * D;
-  const float* Kh = K + base;
-  const float* Vh = V + base;
+  // workgroup -> (head, key range, query tile)
+  const int tile = xcd_remap(blockIdx.x, a.total);
+  const int hs = tile / a.qtiles;
+  const int qt = tile - hs * a.qtiles;
+  const int bh = hs / a.splits;
+  const int sp = hs - bh * a.splits;
+  const int key0 = sp * a.split_len;            // first key of this range
+  const int n = min(a.n_k - key0, a.split_len);  // keys of this range
+  const int n_q = a.n_q;
+  const double C64 = a.C64;
+  const float* Kh = a.K + ((int64_t)bh * a.n_k + key0) * D;
+  const float* Vh = a.V + ((int64_t)bh * a.n_k + key0) * D;
   const int row = qt * kBQ + wave * 16 + l16;  // this lane's query row
+  const int64_t grow = (int64_t)bh * n_q + row;
 
   // B operand of S^T = K Q^T: Q[row][4*kk + g4] as fp64
   double qd[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
-    qd[kk] = row < n ? (double)Q[base + (int64_t)row * D + 4 * kk + g4] : 0.0;
+    qd[kk] = row < n_q ? (double)a.Q[grow * D + 4 * kk + g4] : 0.0;
 
   double m_run = -INFINITY;  // running max of raw scores (fp64)
   float l_run = 0.f;         // this lane's share of the running sum
@@ -173,40 +202,61 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
   float l_tot = l_run + xor16f(l_run);
   l_tot = l_tot + xor32(l_tot);
   const float inv = 1.f / l_tot;
-  if (row < n) {
+  if (row < n_q) {
     // acc[db] register r holds O[row][16*db + 4*g4 + r]
-    float* orow = O + base + (int64_t)row * D;
+    const int64_t orow_idx = a.Po == nullptr ? grow : (int64_t)sp * a.rows + grow;
+    float* orow = (a.Po == nullptr ? a.O : a.Po) + orow_idx * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       f32x4 w = acc[db] * inv;
       *reinterpret_cast<f32x4*>(orow + db * 16 + 4 * g4) = w;
     }
-    if (Mx != nullptr && g4 == 0) {
-      Mx[(int64_t)bh * n + row] = (float)(m_run * scale64);
-      Ls[(int64_t)bh * n + row] = l_tot;
+    if (g4 == 0) {
+      if (a.Po != nullptr) {
+        float* rec = a.Ps + orow_idx * 4;
+        *reinterpret_cast<double*>(rec) = m_run;
+        rec[2] = l_tot;
+        rec[3] = 0.f;
+      } else if (a.Mx != nullptr) {
+        a.Mx[grow] = (float)(m_run * a.scale64);
+        a.Ls[grow] = l_tot;
+      }
     }
   }
 }
 
 template <int D>
-hipError_t launch(int64_t BH, int n, const void* q, const void* k, const void* v, void* o,
-                  float* m, float* l, hipStream_t stream) {
-  const int qtiles = (n + kBQ - 1) / kBQ;
-  const int64_t total = BH * qtiles;
-  const double scale64 = 1.0 / sqrt((double)D);
-  const double C64 = 1.4426950408889634 * scale64;
-  hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)total), dim3(kThreads), 0, stream,
-                     (const float*)q, (const float*)k, (const float*)v, (float*)o, m, l, n, qtiles,
-                     (int)total, C64, scale64);
+hipError_t launch(const FwdProblem& p, hipStream_t stream) {
+  FwdArgs32 a;
+  a.Q = static_cast<const float*>(p.q);
+  a.K = static_cast<const float*>(p.k);
+  a.V = static_cast<const float*>(p.v);
+  a.O = static_cast<float*>(p.o);
+  a.Mx = p.m;
+  a.Ls = p.l;
+  a.rows = p.heads * p.rows_q;
+  a.n_q = p.rows_q;
+  a.n_k = p.n_k;
+  a.qtiles = (p.rows_q + kBQ - 1) / kBQ;
+  a.splits = p.splits > 1 ? p.splits : 1;
+  a.split_len = p.splits > 1 ? p.split_len : p.n_k;
+  a.Po = p.splits > 1 ? p.part : nullptr;
+  a.Ps = p.splits > 1 ? p.part + (int64_t)a.splits * a.rows * D : nullptr;
+  const int64_t total = p.heads * a.splits * a.qtiles;
+  a.total = (int)total;
+  a.scale64 = 1.0 / sqrt((double)D);
+  a.C64 = 1.4426950408889634 * a.scale64;
+  hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)total), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fwd_f32(int d, int64_t BH, int n, const void* q, const void* k, const void* v,
-                          void* o, float* m, float* l, hipStream_t stream) {
-  if (d == 64) return launch<64>(BH, n, q, k, v, o, m, l, stream);
-  return launch<128>(BH, n, q, k, v, o, m, l, stream);
+FwdGeometry fwd_geometry_f32(int) { return FwdGeometry{kBQ, kBC}; }
+
+hipError_t launch_fwd_f32(int d, const FwdProblem& p, hipStream_t stream) {
+  if (d == 64) return launch<64>(p, stream);
+  return launch<128>(p, stream);
 }
 
 }  // namespace mea

@@ -2,6 +2,7 @@
 // the host, then dispatch to the gfx950 kernels on the caller's stream.
 // Validation never calls HIP, so every error path can be exercised without a
 // GPU. The library allocates nothing and keeps no state.
+#include <algorithm>
 #include <climits>
 #include <cstdint>
 
@@ -10,23 +11,54 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
-// Largest grid the kernels are launched with is B*H*ceil(n/64) workgroups of
-// 256 threads; keep it (and all row indices) comfortably inside 32 bits.
+constexpr int kVersion = 200;  // 0.2.0
+// The largest grids are (heads * ceil(rows/64)) workgroups of 256 threads;
+// keep them (and all row indices) comfortably inside 32 bits.
 constexpr int64_t kMaxN = int64_t(1) << 24;
 constexpr int64_t kMaxBH = int64_t(1) << 24;
 constexpr int64_t kMaxBlocks = int64_t(1) << 23;
+// Split-key planning: at most this many key ranges per head; the automatic
+// choice aims at this many workgroups (four per compute unit) and keeps at
+// least two key tiles in every range.
+constexpr int64_t kMaxSplits = 256;
+constexpr int64_t kAutoWorkgroups = 1024;
+constexpr int64_t kAutoMinTiles = 2;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-mea_status_t check_common(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d, bool* empty) {
+// A validated problem: `heads` = B * H_kv, `rows_q` = G * n_q (see mea_launch.h).
+struct Shape {
+  bool bf16 = false;
+  int d = 0;
+  int64_t heads = 0;
+  int64_t rows_q = 0;
+  int64_t n_k = 0;
+  int64_t q_rows_total = 0;  // B * H * n_q
+  bool empty = false;        // nothing to compute
+};
+
+mea_status_t check_shape(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_t n_q,
+                         int64_t n_k, int64_t d, Shape* s) {
   if (dt != MEA_DTYPE_F32 && dt != MEA_DTYPE_BF16) return MEA_ERR_UNSUPPORTED;
-  if (B < 0 || H < 0 || n < 0 || d < 0) return MEA_ERR_SHAPE;
-  if (n > kMaxN) return MEA_ERR_SHAPE;
+  if (B < 0 || H < 0 || H_kv < 0 || n_q < 0 || n_k < 0 || d < 0) return MEA_ERR_SHAPE;
+  if (H > 0 && (H_kv == 0 || H % H_kv != 0)) return MEA_ERR_SHAPE;
+  if (n_q > kMaxN || n_k > kMaxN) return MEA_ERR_SHAPE;
   if (H != 0 && B > kMaxBH / H) return MEA_ERR_SHAPE;
-  if (B != 0 && H != 0 && B * H * ((n + 63) / 64) > kMaxBlocks) return MEA_ERR_SHAPE;
+  const int64_t G = H > 0 ? H / H_kv : 1;
+  if (G * n_q > kMaxN) return MEA_ERR_SHAPE;
+  const int64_t heads = B * (H > 0 ? H_kv : 0);
+  if (heads != 0 && heads * std::max(cdiv(G * n_q, 64), cdiv(n_k, 64)) > kMaxBlocks)
+    return MEA_ERR_SHAPE;
   if (d != 64 && d != 128) return MEA_ERR_UNSUPPORTED;
-  *empty = (B == 0 || H == 0 || n == 0);
+  s->bf16 = dt == MEA_DTYPE_BF16;
+  s->d = (int)d;
+  s->heads = heads;
+  s->rows_q = G * n_q;
+  s->n_k = n_k;
+  s->q_rows_total = B * H * n_q;
+  s->empty = heads == 0 || (n_q == 0 && n_k == 0);
   return MEA_OK;
 }
 
@@ -36,6 +68,124 @@ mea_status_t check_ptrs(std::initializer_list<const void*> ptrs) {
   for (const void* p : ptrs)
     if (!aligned16(p)) return MEA_ERR_ALIGN;
   return MEA_OK;
+}
+
+// Forward-only shape rules: no query rows is a no-op; queries without keys
+// have no softmax.
+mea_status_t check_fwd_shape(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_t n_q,
+                             int64_t n_k, int64_t d, Shape* s) {
+  mea_status_t st = check_shape(dt, B, H, H_kv, n_q, n_k, d, s);
+  if (st != MEA_OK) return st;
+  if (s->rows_q == 0) s->empty = true;
+  if (!s->empty && n_k == 0) return MEA_ERR_SHAPE;
+  return MEA_OK;
+}
+
+struct SplitPlan {
+  int64_t splits = 1;
+  int64_t split_len = 0;
+};
+
+SplitPlan plan_splits(const Shape& s, int64_t requested) {
+  SplitPlan p;
+  p.split_len = s.n_k;
+  if (s.empty || s.n_k == 0) return p;
+  const mea::FwdGeometry g = mea::fwd_geometry(s.bf16, s.d);
+  const int64_t tiles_k = cdiv(s.n_k, g.key_tile);
+  int64_t want = requested;
+  if (want <= 0) {
+    const int64_t base = s.heads * cdiv(s.rows_q, g.query_rows);
+    want = std::min(cdiv(kAutoWorkgroups, base), std::max<int64_t>(1, tiles_k / kAutoMinTiles));
+  }
+  want = std::max<int64_t>(1, std::min({want, tiles_k, kMaxSplits}));
+  p.split_len = cdiv(tiles_k, want) * g.key_tile;  // whole key tiles per range
+  p.splits = cdiv(s.n_k, p.split_len);             // every range non-empty
+  if (p.splits == 1) p.split_len = s.n_k;
+  return p;
+}
+
+size_t split_workspace_bytes(const Shape& s, const SplitPlan& p) {
+  if (p.splits <= 1) return 0;
+  return (size_t)(p.splits * s.heads * s.rows_q * (s.d + 4) * 4);
+}
+
+mea::FwdProblem fwd_problem(const Shape& s, const void* q, const void* k, const void* v, void* o,
+                            float* row_max, float* row_sum) {
+  mea::FwdProblem p;
+  p.heads = s.heads;
+  p.rows_q = (int)s.rows_q;
+  p.n_k = (int)s.n_k;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.m = row_max;
+  p.l = row_sum;
+  return p;
+}
+
+hipError_t run_fwd(const Shape& s, const mea::FwdProblem& p, hipStream_t stream) {
+  return s.bf16 ? mea::launch_fwd_bf16(s.d, p, stream) : mea::launch_fwd_f32(s.d, p, stream);
+}
+
+mea_status_t fwd_impl(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_t n_q,
+                      int64_t n_k, int64_t d, const void* q, const void* k, const void* v,
+                      void* o, float* row_max, float* row_sum, void* stream) {
+  Shape s;
+  mea_status_t st = check_fwd_shape(dt, B, H, H_kv, n_q, n_k, d, &s);
+  if (st != MEA_OK || s.empty) return st;
+  if ((row_max == nullptr) != (row_sum == nullptr)) return MEA_ERR_NULL;
+  st = check_ptrs({q, k, v, o});
+  if (st != MEA_OK) return st;
+  if (row_max != nullptr && (!aligned16(row_max) || !aligned16(row_sum))) return MEA_ERR_ALIGN;
+  hipError_t e = run_fwd(s, fwd_problem(s, q, k, v, o, row_max, row_sum),
+                         reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MEA_OK : MEA_ERR_LAUNCH;
+}
+
+mea_status_t bwd_impl(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_t n_q,
+                      int64_t n_k, int64_t d, const void* q, const void* k, const void* v,
+                      const void* o, const void* dO, const float* row_max, const float* row_sum,
+                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  Shape s;
+  mea_status_t st = check_shape(dt, B, H, H_kv, n_q, n_k, d, &s);
+  if (st != MEA_OK || s.empty) return st;
+  if (n_k == 0) return MEA_ERR_SHAPE;  // query rows without keys have no forward
+  if (dt != MEA_DTYPE_BF16) return MEA_ERR_UNSUPPORTED;
+  // without query rows only the key side is touched (dk = dv = 0)
+  st = s.rows_q > 0 ? check_ptrs({q, k, v, o, dO, row_max, row_sum, dq, dk, dv})
+                    : check_ptrs({k, v, dk, dv});
+  if (st != MEA_OK) return st;
+  const size_t need = (size_t)(8 * s.q_rows_total);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return MEA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MEA_ERR_ALIGN;
+  }
+  mea::BwdProblem p;
+  p.heads = s.heads;
+  p.rows_q = (int)s.rows_q;
+  p.n_k = (int)s.n_k;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dO = dO;
+  p.m = row_max;
+  p.l = row_sum;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.ws = static_cast<float*>(workspace);
+  hipError_t e = mea::launch_bwd_bf16(s.d, p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MEA_OK : MEA_ERR_LAUNCH;
+}
+
+size_t bwd_ws_bytes(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_t n_q, int64_t n_k,
+                    int64_t d) {
+  Shape s;
+  if (check_shape(dt, B, H, H_kv, n_q, n_k, d, &s) != MEA_OK || s.empty) return 0;
+  return (size_t)(8 * s.q_rows_total);
 }
 
 }  // namespace
@@ -60,24 +210,22 @@ int mea_version(void) { return kVersion; }
 mea_status_t attn_fwd(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d,
                       const void* q, const void* k, const void* v, void* o,
                       float* row_max, float* row_sum, void* stream) {
-  bool empty = false;
-  mea_status_t st = check_common(dt, B, H, n, d, &empty);
-  if (st != MEA_OK || empty) return st;
-  if ((row_max == nullptr) != (row_sum == nullptr)) return MEA_ERR_NULL;
-  st = check_ptrs({q, k, v, o});
-  if (st != MEA_OK) return st;
-  if (row_max != nullptr && (!aligned16(row_max) || !aligned16(row_sum))) return MEA_ERR_ALIGN;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = dt == MEA_DTYPE_BF16
-                     ? mea::launch_fwd_bf16((int)d, B * H, (int)n, q, k, v, o, row_max, row_sum, s)
-                     : mea::launch_fwd_f32((int)d, B * H, (int)n, q, k, v, o, row_max, row_sum, s);
-  return e == hipSuccess ? MEA_OK : MEA_ERR_LAUNCH;
+  return fwd_impl(dt, B, H, H, n, n, d, q, k, v, o, row_max, row_sum, stream);
+}
+
+mea_status_t attn_fwd_ex(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_t n_q,
+                         int64_t n_k, int64_t d, const void* q, const void* k, const void* v,
+                         void* o, float* row_max, float* row_sum, void* stream) {
+  return fwd_impl(dt, B, H, H_kv, n_q, n_k, d, q, k, v, o, row_max, row_sum, stream);
 }
 
 size_t attn_bwd_workspace_bytes(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d) {
-  bool empty = false;
-  if (check_common(dt, B, H, n, d, &empty) != MEA_OK || empty) return 0;
-  return (size_t)(8 * B * H * n);
+  return bwd_ws_bytes(dt, B, H, H, n, n, d);
+}
+
+size_t attn_bwd_ex_workspace_bytes(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv,
+                                   int64_t n_q, int64_t n_k, int64_t d) {
+  return bwd_ws_bytes(dt, B, H, H_kv, n_q, n_k, d);
 }
 
 mea_status_t attn_bwd(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d,
@@ -85,17 +233,65 @@ mea_status_t attn_bwd(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d
                       const void* dO, const float* row_max, const float* row_sum,
                       void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                       void* stream) {
-  bool empty = false;
-  mea_status_t st = check_common(dt, B, H, n, d, &empty);
-  if (st != MEA_OK || empty) return st;
-  if (dt != MEA_DTYPE_BF16) return MEA_ERR_UNSUPPORTED;
-  st = check_ptrs({q, k, v, o, dO, row_max, row_sum, dq, dk, dv});
+  return bwd_impl(dt, B, H, H, n, n, d, q, k, v, o, dO, row_max, row_sum, dq, dk, dv, workspace,
+                  workspace_bytes, stream);
+}
+
+mea_status_t attn_bwd_ex(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_t n_q,
+                         int64_t n_k, int64_t d, const void* q, const void* k, const void* v,
+                         const void* o, const void* dO, const float* row_max,
+                         const float* row_sum, void* dq, void* dk, void* dv, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return bwd_impl(dt, B, H, H_kv, n_q, n_k, d, q, k, v, o, dO, row_max, row_sum, dq, dk, dv,
+                  workspace, workspace_bytes, stream);
+}
+
+int64_t attn_fwd_splitkv_num_splits(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv,
+                                    int64_t n_q, int64_t n_k, int64_t d, int64_t num_splits) {
+  Shape s;
+  if (num_splits < 0 || check_fwd_shape(dt, B, H, H_kv, n_q, n_k, d, &s) != MEA_OK) return 0;
+  if (s.empty) return 1;
+  return plan_splits(s, num_splits).splits;
+}
+
+size_t attn_fwd_splitkv_workspace_bytes(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv,
+                                        int64_t n_q, int64_t n_k, int64_t d, int64_t num_splits) {
+  Shape s;
+  if (num_splits < 0 || check_fwd_shape(dt, B, H, H_kv, n_q, n_k, d, &s) != MEA_OK || s.empty)
+    return 0;
+  return split_workspace_bytes(s, plan_splits(s, num_splits));
+}
+
+mea_status_t attn_fwd_splitkv(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_t n_q,
+                              int64_t n_k, int64_t d, const void* q, const void* k, const void* v,
+                              void* o, float* row_max, float* row_sum, int64_t num_splits,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  mea_status_t st = check_fwd_shape(dt, B, H, H_kv, n_q, n_k, d, &s);
   if (st != MEA_OK) return st;
-  if (workspace == nullptr || workspace_bytes < (size_t)(8 * B * H * n)) return MEA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return MEA_ERR_ALIGN;
-  hipError_t e = mea::launch_bwd_bf16((int)d, B * H, (int)n, q, k, v, o, dO, row_max, row_sum,
-                                      dq, dk, dv, static_cast<float*>(workspace),
-                                      reinterpret_cast<hipStream_t>(stream));
+  if (num_splits < 0) return MEA_ERR_SHAPE;
+  if (s.empty) return MEA_OK;
+  if ((row_max == nullptr) != (row_sum == nullptr)) return MEA_ERR_NULL;
+  st = check_ptrs({q, k, v, o});
+  if (st != MEA_OK) return st;
+  if (row_max != nullptr && (!aligned16(row_max) || !aligned16(row_sum))) return MEA_ERR_ALIGN;
+  const SplitPlan plan = plan_splits(s, num_splits);
+  if (s.heads * plan.splits * cdiv(s.rows_q, mea::fwd_geometry(s.bf16, s.d).query_rows) > kMaxBlocks)
+    return MEA_ERR_SHAPE;
+  const size_t need = split_workspace_bytes(s, plan);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return MEA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MEA_ERR_ALIGN;
+  }
+  hipStream_t stream_h = reinterpret_cast<hipStream_t>(stream);
+  mea::FwdProblem p = fwd_problem(s, q, k, v, o, row_max, row_sum);
+  if (plan.splits > 1) {
+    p.splits = (int)plan.splits;
+    p.split_len = (int)plan.split_len;
+    p.part = static_cast<float*>(workspace);
+  }
+  hipError_t e = run_fwd(s, p, stream_h);
+  if (e == hipSuccess && plan.splits > 1) e = mea::launch_merge(s.bf16, s.d, p, stream_h);
   return e == hipSuccess ? MEA_OK : MEA_ERR_LAUNCH;
 }
 

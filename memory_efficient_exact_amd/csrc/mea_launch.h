@@ -1,6 +1,14 @@
 // Internal launcher declarations shared by the C-ABI layer and the kernel
 // translation units. Shapes arrive already validated; every launcher enqueues
 // on `stream` and returns the hipGetLastError() code of its launches.
+//
+// Heads as the kernels see them. Query heads that share one key/value head
+// (grouped-query attention) are adjacent in a [B, H, n_q, d] tensor, so the
+// G = H / H_kv query heads of a group form one contiguous block of G * n_q
+// rows. The kernels therefore work on `heads` = B * H_kv independent
+// problems, each with `rows_q` = G * n_q query rows against `n_k` keys; row r
+// of problem h is query row r % n_q of query head h * G + r / n_q. With
+// H_kv = H this is plain multi-head attention.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -8,17 +16,58 @@
 
 namespace mea {
 
-// bf16 forward: q, k, v, o bf16 [BH, n, d]; m, l fp32 [BH, n] or both null.
-hipError_t launch_fwd_bf16(int d, int64_t BH, int n, const void* q, const void* k, const void* v,
-                           void* o, float* m, float* l, hipStream_t stream);
+struct FwdProblem {
+  int64_t heads = 0;  // B * H_kv
+  int rows_q = 0;     // G * n_q query rows per head
+  int n_k = 0;        // keys per head
+  const void* q = nullptr;  // [heads, rows_q, d]
+  const void* k = nullptr;  // [heads, n_k, d]
+  const void* v = nullptr;  // [heads, n_k, d]
+  void* o = nullptr;        // [heads, rows_q, d]; written by the final pass
+  float* m = nullptr;       // [heads, rows_q] row max (natural units) or null
+  float* l = nullptr;       // [heads, rows_q] row sum or null (null iff m is)
+  // Split-key mode (splits > 1): key range s = [s * split_len, min(n_k, (s+1) * split_len))
+  // of every head is reduced by its own workgroups into `part`, then a merge
+  // pass writes o, m, l. Layout of part (fp32): partial outputs
+  // [splits][heads * rows_q][d], then one 16-byte record per (split, row).
+  int splits = 1;
+  int split_len = 0;
+  float* part = nullptr;
+};
 
-// fp32 forward (fp64 scores): same layout with fp32 elements.
-hipError_t launch_fwd_f32(int d, int64_t BH, int n, const void* q, const void* k, const void* v,
-                          void* o, float* m, float* l, hipStream_t stream);
+// Tile geometry of the forward kernels, for planning the key splits.
+struct FwdGeometry {
+  int query_rows;  // query rows per workgroup
+  int key_tile;    // keys per LDS tile (split lengths are multiples of it)
+};
+FwdGeometry fwd_geometry_bf16(int d);
+FwdGeometry fwd_geometry_f32(int d);
+inline FwdGeometry fwd_geometry(bool bf16, int d) { return bf16 ? fwd_geometry_bf16(d) : fwd_geometry_f32(d); }
 
-// bf16 backward: three kernels (row preprocess, dK/dV, dQ). ws holds 2*BH*n floats.
-hipError_t launch_bwd_bf16(int d, int64_t BH, int n, const void* q, const void* k, const void* v,
-                           const void* o, const void* dO, const float* m, const float* l,
-                           void* dq, void* dk, void* dv, float* ws, hipStream_t stream);
+// Forward pass (final or, with p.splits > 1, partial) for bf16 / fp32 inputs.
+hipError_t launch_fwd_bf16(int d, const FwdProblem& p, hipStream_t stream);
+hipError_t launch_fwd_f32(int d, const FwdProblem& p, hipStream_t stream);
+// Merge of the split partials in p.part into p.o, p.m, p.l.
+hipError_t launch_merge(bool bf16, int d, const FwdProblem& p, hipStream_t stream);
+
+struct BwdProblem {
+  int64_t heads = 0;  // B * H_kv
+  int rows_q = 0;     // G * n_q
+  int n_k = 0;
+  const void* q = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const void* o = nullptr;
+  const void* dO = nullptr;
+  const float* m = nullptr;
+  const float* l = nullptr;
+  void* dq = nullptr;
+  void* dk = nullptr;  // [heads, n_k, d]: sums over the query heads of each group
+  void* dv = nullptr;
+  float* ws = nullptr;  // 2 * heads * rows_q floats
+};
+
+// bf16 backward: row preprocess, then one grid with dK/dV and dQ workgroups.
+hipError_t launch_bwd_bf16(int d, const BwdProblem& p, hipStream_t stream);
 
 }  // namespace mea

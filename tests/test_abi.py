@@ -7,6 +7,7 @@ without a GPU. No test in this file launches a kernel.
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 import torch
@@ -22,9 +23,14 @@ A = 0x10000  # aligned fake device addresses: validation never dereferences them
 
 
 def header_functions():
+    """Names of the functions include/mea.h declares (every one is marked MEA_API)."""
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "sizeof"})
+    names = re.findall(r"^MEA_API\b[^;(]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    # every prototype in the header carries the export marker
+    protos = re.findall(r"^[A-Za-z_][^;{}#]*?\b([a-z_][a-z0-9_]*)\s*\([^;{}]*\)\s*;", text, flags=re.M)
+    assert sorted(set(protos)) == sorted(set(names)), (protos, names)
+    return sorted(set(names))
 
 
 @pytest.fixture(scope="module")
@@ -36,9 +42,19 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert set(names) >= {"attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str", "mea_version"}
+    assert set(names) >= {"attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
+                          "mea_version", "attn_fwd_ex", "attn_bwd_ex", "attn_bwd_ex_workspace_bytes",
+                          "attn_fwd_splitkv", "attn_fwd_splitkv_num_splits",
+                          "attn_fwd_splitkv_workspace_bytes"}
     for nm in names:
         assert hasattr(L, nm), f"libmea.so does not export {nm}"
+
+
+def test_exports_nothing_but_the_c_abi():
+    out = subprocess.run(["nm", "-D", "--defined-only", mea.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.split()[1:2] == ["T"]}
+    assert exported == set(header_functions()), exported ^ set(header_functions())
 
 
 def test_status_strings(L):
@@ -46,7 +62,7 @@ def test_status_strings(L):
                                  "MEA_ERR_ALIGN", "MEA_ERR_WORKSPACE", "MEA_ERR_LAUNCH"]):
         assert mea.attn_status_str(code) == name
     assert mea.attn_status_str(99) == "MEA_UNKNOWN_STATUS"
-    assert mea.mea_version() == 100
+    assert mea.mea_version() == 200
 
 
 def fwd(L, dt=BF16, B=1, H=1, n=128, d=64, q=A, k=A, v=A, o=A, m=0, l=0):
@@ -123,3 +139,118 @@ def test_product_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert not re.search(r"\boracle\b", text), f"{f} mentions the oracle"
     assert not re.search(r"\boracle\b", open(HEADER).read())
+
+
+# ------------------------------------------------------------- _ex entry points
+
+def fwd_ex(L, dt=BF16, B=1, H=4, H_kv=2, n_q=16, n_k=128, d=64, q=A, k=A, v=A, o=A, m=0, l=0):
+    return L.attn_fwd_ex(dt, B, H, H_kv, n_q, n_k, d, q, k, v, o, m, l, None)
+
+
+def bwd_ex(L, dt=BF16, B=1, H=4, H_kv=2, n_q=16, n_k=128, d=64, ptrs=None, ws=A, wsb=1 << 20):
+    p = dict(q=A, k=A, v=A, o=A, do=A, m=A, l=A, dq=A, dk=A, dv=A)
+    p.update(ptrs or {})
+    return L.attn_bwd_ex(dt, B, H, H_kv, n_q, n_k, d, p["q"], p["k"], p["v"], p["o"], p["do"],
+                         p["m"], p["l"], p["dq"], p["dk"], p["dv"], ws, wsb, None)
+
+
+def test_fwd_ex_validation(L):
+    assert fwd_ex(L, dt=3) == UNSUP
+    assert fwd_ex(L, H_kv=3) == SHAPE          # 4 query heads cannot form 3 groups
+    assert fwd_ex(L, H_kv=0) == SHAPE
+    assert fwd_ex(L, H_kv=-2) == SHAPE
+    assert fwd_ex(L, n_q=-1) == SHAPE
+    assert fwd_ex(L, n_k=-1) == SHAPE
+    assert fwd_ex(L, n_k=(1 << 24) + 1) == SHAPE
+    assert fwd_ex(L, H=8, H_kv=1, n_q=(1 << 22)) == SHAPE   # G * n_q rows > 2^24
+    assert fwd_ex(L, n_k=0) == SHAPE           # queries but no keys
+    assert fwd_ex(L, d=80) == UNSUP
+    assert fwd_ex(L, k=0) == NULL
+    assert fwd_ex(L, m=A) == NULL
+    assert fwd_ex(L, o=A + 4) == ALIGN
+    # no query rows: nothing to do, pointers may be NULL
+    assert fwd_ex(L, n_q=0, n_k=0, q=0, k=0, v=0, o=0) == OK
+    assert fwd_ex(L, n_q=0, q=0, k=0, v=0, o=0) == OK
+    assert fwd_ex(L, B=0, q=0, k=0, v=0, o=0) == OK
+    assert fwd_ex(L, H=0, H_kv=0, q=0, k=0, v=0, o=0) == OK
+
+
+def test_bwd_ex_validation(L):
+    assert bwd_ex(L, dt=F32) == UNSUP
+    assert bwd_ex(L, H_kv=3) == SHAPE
+    assert bwd_ex(L, n_k=0) == SHAPE
+    for name in ("q", "k", "v", "o", "do", "m", "l", "dq", "dk", "dv"):
+        assert bwd_ex(L, ptrs={name: 0}) == NULL, name
+        assert bwd_ex(L, ptrs={name: A + 2}) == ALIGN, name
+    need = 8 * 1 * 4 * 16  # 8 bytes per query row of every query head
+    assert mea.attn_bwd_ex_workspace_bytes(BF16, 1, 4, 2, 16, 128, 64) == need
+    assert bwd_ex(L, wsb=need - 1) == WS
+    assert bwd_ex(L, ws=0) == WS
+    assert bwd_ex(L, wsb=need, ws=A + 8) == ALIGN
+    assert bwd_ex(L, B=0, ws=0, wsb=0) == OK
+    assert bwd_ex(L, n_q=0, n_k=0, ws=0, wsb=0) == OK
+    # no query rows: only the key side is checked; no workspace needed
+    q_side = {nm: 0 for nm in ("q", "o", "do", "m", "l", "dq")}
+    assert bwd_ex(L, n_q=0, ptrs=dict(q_side, dk=0), ws=0, wsb=0) == NULL
+
+
+def test_ex_workspace_bytes(L):
+    assert mea.attn_bwd_ex_workspace_bytes(BF16, 2, 32, 8, 100, 7000, 128) == 8 * 2 * 32 * 100
+    assert mea.attn_bwd_ex_workspace_bytes(BF16, 2, 32, 5, 100, 7000, 128) == 0
+    assert mea.attn_bwd_ex_workspace_bytes(BF16, 2, 32, 8, 0, 0, 128) == 0
+
+
+# ---------------------------------------------------------- split-key entry point
+
+def split(L, dt=BF16, B=1, H=1, H_kv=1, n_q=1, n_k=16384, d=64, q=A, k=A, v=A, o=A, m=0, l=0,
+          s=0, ws=A, wsb=1 << 30):
+    return L.attn_fwd_splitkv(dt, B, H, H_kv, n_q, n_k, d, q, k, v, o, m, l, s, ws, wsb, None)
+
+
+@pytest.mark.parametrize("dt,d,tile", [(BF16, 64, 128), (BF16, 128, 64), (F32, 64, 32), (F32, 128, 32)])
+def test_split_planning(L, dt, d, tile):
+    ns = mea.attn_fwd_splitkv_num_splits
+    wsb = mea.attn_fwd_splitkv_workspace_bytes
+    # explicit requests: honoured up to one range per key tile and 256 ranges
+    assert ns(dt, 1, 1, 1, 1, 4096, d, 1) == 1
+    assert ns(dt, 1, 1, 1, 1, 4096, d, 4) == 4
+    assert ns(dt, 1, 1, 1, 1, 4096, d, 10 ** 6) == min(256, 4096 // tile)
+    assert ns(dt, 1, 1, 1, 1, tile, d, 8) == 1          # one key tile: one range
+    assert ns(dt, 1, 1, 1, 1, 3 * tile + 1, d, 3) == 2  # ranges of whole tiles, none empty
+    # automatic choice: a single query against many keys is split; a full grid is not
+    assert ns(dt, 1, 1, 1, 1, 1 << 16, d, 0) > 1
+    assert ns(dt, 64, 64, 64, 4096, 4096, d, 0) == 1
+    # workspace: splits * rows * (d + 4) * 4 bytes, 0 when unsplit
+    s = ns(dt, 2, 8, 2, 5, 4096, d, 4)
+    assert s == 4 and wsb(dt, 2, 8, 2, 5, 4096, d, 4) == 4 * 2 * 8 * 5 * (d + 4) * 4
+    assert wsb(dt, 2, 8, 2, 5, 4096, d, 1) == 0
+    assert ns(dt, 1, 1, 1, 1, 4096, d, -1) == 0
+    assert wsb(dt, 1, 1, 1, 1, 4096, d, -1) == 0
+    assert ns(dt, 1, 3, 2, 1, 4096, d, 0) == 0           # invalid grouping
+
+
+def test_split_validation(L):
+    need = mea.attn_fwd_splitkv_workspace_bytes(BF16, 1, 1, 1, 1, 16384, 64, 0)
+    assert need > 0
+    assert split(L, wsb=need - 1) == WS
+    assert split(L, ws=0) == WS
+    assert split(L, ws=A + 4, wsb=need) == ALIGN
+    assert split(L, s=-1) == SHAPE
+    assert split(L, H=3, H_kv=2) == SHAPE
+    assert split(L, n_k=0) == SHAPE
+    assert split(L, dt=7) == UNSUP
+    assert split(L, q=0) == NULL
+    assert split(L, m=A) == NULL
+    # empty problems: OK without touching anything
+    assert split(L, n_q=0, q=0, k=0, v=0, o=0, ws=0, wsb=0) == OK
+    # one range needs no workspace
+    assert split(L, n_k=100, s=1, ws=0, wsb=0, q=0) == NULL  # pointer checks still run
+
+
+def test_binding_rejects_bad_group_shapes():
+    q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 9, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mea.attn_fwd_ex(q, k, k)  # CPU tensors
+    with pytest.raises(ValueError):
+        mea.attn_fwd_splitkv(q, k, k[..., :32])

@@ -1,0 +1,161 @@
+"""GPU parity for grouped-query heads, separate query/key lengths and the
+split-key forward, through the C ABI, against the fp64 oracle.
+
+Tolerances are those of test_gpu_parity.py (fp32: 1e-5; bf16: 2e-2 plus
+relative L2 <= 1e-2), element by element on the same seeded inputs. The
+oracle's ``gqa_fwd``/``gqa_bwd`` give query head h the key/value head
+h // (H / H_kv) and ``split_fwd`` is pinned to ``naive_fwd``; here the GPU is
+compared with the plain definitions directly.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import inputgen
+import memory_efficient_exact_amd as mea
+import oracle
+
+from test_gpu_parity import check, check_stats, f64, gpu, say
+
+pytestmark = pytest.mark.gpu
+
+# (B, H, H_kv, n_q, n_k): grouped, multi-query, cross lengths, ragged tiles, a single key
+GQA_CASES = [(1, 4, 2, 17, 300), (2, 8, 1, 5, 129), (1, 6, 3, 257, 64), (1, 2, 2, 1, 1000),
+             (1, 3, 3, 300, 1), (1, 4, 4, 100, 33), (2, 8, 2, 64, 513)]
+
+
+def draw(B, H, H_kv, n_q, n_k, d, dtype, seed, with_do=False, qk_scale=1.0):
+    return inputgen.draw_gqa(B, H, H_kv, n_q, n_k, d, dtype, seed=seed, with_do=with_do,
+                             qk_scale=qk_scale)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,H_kv,n_q,n_k", GQA_CASES)
+def test_fwd_ex_small_full(dtype, d, B, H, H_kv, n_q, n_k):
+    say("fwd_ex", dtype, d, B, H, H_kv, n_q, n_k)
+    t = draw(B, H, H_kv, n_q, n_k, d, dtype, seed=21 + n_q + n_k + d)
+    o, m, l = mea.attn_fwd_ex(gpu(t["q"]), gpu(t["k"]), gpu(t["v"]))
+    torch.cuda.synchronize()
+    o_ref, m_ref, l_ref = oracle.gqa_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]))
+    check("O", f64(o.cpu()), o_ref, dtype)
+    check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, dtype)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,H_kv,n_q,n_k", [(1, 4, 2, 17, 300), (1, 8, 1, 33, 129),
+                                              (2, 4, 4, 100, 37), (1, 2, 1, 1, 200),
+                                              (1, 4, 2, 300, 1), (1, 6, 2, 130, 260)])
+def test_bwd_ex_small_full(d, B, H, H_kv, n_q, n_k):
+    say("bwd_ex", d, B, H, H_kv, n_q, n_k)
+    t = draw(B, H, H_kv, n_q, n_k, d, "bf16", seed=31 + n_q + n_k + d, with_do=True)
+    q, k, v, do = (gpu(t[x]) for x in ("q", "k", "v", "do"))
+    o, m, l = mea.attn_fwd_ex(q, k, v)
+    dq, dk, dv = mea.attn_bwd_ex(q, k, v, o, do, m, l)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.gqa_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]))
+    check("dQ", f64(dq.cpu()), rq, "bf16")
+    check("dK", f64(dk.cpu()), rk, "bf16")
+    check("dV", f64(dv.cpu()), rv, "bf16")
+
+
+def test_bwd_ex_without_queries_gives_zero_key_gradients():
+    say("bwd_ex n_q=0")
+    t = draw(1, 4, 2, 0, 200, 64, "bf16", seed=41, with_do=True)
+    q, k, v, do = (gpu(t[x]) for x in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    m = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    l = torch.empty_like(m)
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    _, dk, dv = mea.attn_bwd_ex(q, k, v, o, do, m, l, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
+# ------------------------------------------------------------------ split keys
+
+SPLIT_CASES = [(1, 1, 1, 1, 2000), (1, 4, 2, 33, 1500), (2, 2, 2, 130, 777), (1, 8, 1, 3, 4100)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 7, 1000])
+@pytest.mark.parametrize("B,H,H_kv,n_q,n_k", SPLIT_CASES)
+def test_splitkv_small_full(dtype, d, splits, B, H, H_kv, n_q, n_k):
+    used = mea.attn_fwd_splitkv_num_splits(mea.DTYPE_BF16 if dtype == "bf16" else mea.DTYPE_F32,
+                                           B, H, H_kv, n_q, n_k, d, splits)
+    say("splitkv", dtype, d, splits, "->", used, B, H, H_kv, n_q, n_k)
+    t = draw(B, H, H_kv, n_q, n_k, d, dtype, seed=51 + n_q + n_k + d)
+    o, m, l = mea.attn_fwd_splitkv(gpu(t["q"]), gpu(t["k"]), gpu(t["v"]), num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, m_ref, l_ref = oracle.gqa_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]))
+    check("O", f64(o.cpu()), o_ref, dtype)
+    check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, dtype)
+
+
+def test_splitkv_workspace_is_reused_across_calls():
+    # the second, smaller call reads nothing the first one left behind
+    say("splitkv workspace reuse")
+    big = draw(1, 2, 1, 40, 3000, 64, "bf16", seed=61)
+    small = draw(1, 2, 1, 9, 700, 64, "bf16", seed=62)
+    need = mea.attn_fwd_splitkv_workspace_bytes(mea.DTYPE_BF16, 1, 2, 1, 40, 3000, 64, 16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for t, s in ((big, 16), (small, 5)):
+        o, m, l = mea.attn_fwd_splitkv(gpu(t["q"]), gpu(t["k"]), gpu(t["v"]), num_splits=s,
+                                       workspace=ws)
+        torch.cuda.synchronize()
+        o_ref, m_ref, l_ref = oracle.gqa_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]))
+        check("O", f64(o.cpu()), o_ref, "bf16")
+        check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, "bf16")
+
+
+def test_splitkv_single_head_fp32_workload_full():
+    # the 1 x 1 x 1024 x 64 fp32 workload: 16 query tiles alone leave most of the GPU idle
+    w = inputgen.WORKLOADS["c1_single_head_fp32"]
+    t = inputgen.make_inputs(w)
+    used = mea.attn_fwd_splitkv_num_splits(mea.DTYPE_F32, w.B, w.H, w.H, w.n, w.n, w.d, 0)
+    say("splitkv", w.name, "splits", used)
+    assert used > 1
+    o, m, l = mea.attn_fwd_splitkv(gpu(t["q"]), gpu(t["k"]), gpu(t["v"]))
+    torch.cuda.synchronize()
+    o_ref, m_ref, l_ref = oracle.naive_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]))
+    check("O", f64(o.cpu()), o_ref, "fp32")
+    check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, "fp32")
+
+
+def test_splitkv_stress_fp32_sampled_rows():
+    # 2 x 8 x 8192 x 128 fp32, Q and K scaled by 30 (scores ~1e4), all-equal keys in head 0:
+    # range maxima differ by thousands, so the merge must re-base every range exactly
+    w = inputgen.WORKLOADS["c4_stress_fp32"]
+    t = inputgen.make_inputs(w)
+    say("splitkv", w.name, "splits 8")
+    o, m, l = mea.attn_fwd_splitkv(gpu(t["q"]), gpu(t["k"]), gpu(t["v"]), num_splits=8)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(71).choice(w.n, 48, replace=False)
+    rows = np.concatenate([rows, [0, w.n - 1]])
+    o_ref, m_ref, l_ref = oracle.naive_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), rows=rows)
+    check("O", f64(o.cpu())[:, :, rows], o_ref, "fp32")
+    check_stats(m.cpu().numpy()[:, :, rows], l.cpu().numpy()[:, :, rows], m_ref, l_ref, "fp32")
+    mean = f64(t["v"])[:, 0].mean(axis=1)  # equal keys: uniform weights
+    check("O equal-key head", f64(o.cpu())[:, 0], np.broadcast_to(mean[:, None, :], (2, w.n, 128)),
+          "fp32")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp32", 128)])
+def test_splitkv_decode_step(dtype, d):
+    # one new query per head against a 16384-entry key/value cache, 4 query heads per K/V head
+    B, H, H_kv, n_q, n_k = 1, 8, 2, 1, 16384
+    dt = mea.DTYPE_BF16 if dtype == "bf16" else mea.DTYPE_F32
+    used = mea.attn_fwd_splitkv_num_splits(dt, B, H, H_kv, n_q, n_k, d, 0)
+    say("decode", dtype, d, "splits", used)
+    assert used >= 16
+    t = draw(B, H, H_kv, n_q, n_k, d, dtype, seed=81)
+    o, m, l = mea.attn_fwd_splitkv(gpu(t["q"]), gpu(t["k"]), gpu(t["v"]))
+    o1, m1, l1 = mea.attn_fwd_ex(gpu(t["q"]), gpu(t["k"]), gpu(t["v"]))
+    torch.cuda.synchronize()
+    o_ref, m_ref, l_ref = oracle.gqa_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]))
+    check("O split", f64(o.cpu()), o_ref, dtype)
+    check("O unsplit", f64(o1.cpu()), o_ref, dtype)
+    check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, dtype)

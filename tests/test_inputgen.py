@@ -49,3 +49,12 @@ def test_workload_table():
     assert w["c3_long_bf16"].fwd_flops() == 4.0 * 16 * 16384 ** 2 * 64
     assert w["c5_train_bf16"].backward and w["c5_train_bf16"].bwd_flops() == 10.0 * 16 * 8192 ** 2 * 64
     assert w["c1_single_head_fp32"].dtype == "fp32" and w["c4_stress_fp32"].d == 128
+
+
+def test_draw_gqa_matches_draw_on_equal_shapes():
+    a = inputgen.draw(2, 3, 17, 64, "bf16", seed=9, qk_scale=2.0, with_do=True)
+    b = inputgen.draw_gqa(2, 3, 3, 17, 17, 64, "bf16", seed=9, qk_scale=2.0, with_do=True)
+    for nm in ("q", "k", "v", "do"):
+        assert torch.equal(a[nm], b[nm]), nm
+    c = inputgen.draw_gqa(1, 4, 2, 5, 9, 64, "fp32", seed=1)
+    assert c["q"].shape == (1, 4, 5, 64) and c["k"].shape == (1, 2, 9, 64) and "do" not in c
