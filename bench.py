@@ -141,17 +141,97 @@ def sweep_configs(steps, warmup):
     return {"mode": "configs", "steps": steps, "warmup": warmup, "rows": rows}
 
 
+# Shapes for the split-key / grouped-query sweep: (name, B, H, H_kv, n_q, n_k, d, dtype, backward).
+# The decoding rows are one new query per head against a long key/value cache
+# with 4 query heads per key/value head, the grouped layout the pages' KV-cache
+# section describes; the prefill row is the same grouping at n_q = n_k.
+SPLIT_CASES = [
+    ("single_head_fp32_1024", 1, 1, 1, 1024, 1024, 64, "fp32", False),
+    ("multihead_bf16_4096", 4, 8, 8, 4096, 4096, 64, "bf16", False),
+    ("decode_gqa_bf16_d128_16k", 1, 32, 8, 1, 16384, 128, "bf16", False),
+    ("decode_gqa_bf16_d128_128k_b4", 4, 32, 8, 1, 131072, 128, "bf16", False),
+    ("decode_gqa_bf16_d64_32k_b8", 8, 32, 8, 1, 32768, 64, "bf16", False),
+    ("decode_gqa_fp32_d128_16k", 1, 32, 8, 1, 16384, 128, "fp32", False),
+    ("prefill_gqa_bf16_d128_8k", 1, 32, 8, 8192, 8192, 128, "bf16", True),
+]
+
+
+def sweep_split(steps, warmup):
+    """Unsplit (attn_fwd_ex) against split-key (attn_fwd_splitkv, automatic
+    split count) forward time on small-grid and decoding shapes, plus the
+    grouped-query backward where the row trains. Decoding is HBM-bound: its
+    compulsory traffic is K and V once per key/value head, Q and O once."""
+    import torch
+
+    import inputgen
+    import memory_efficient_exact_amd as mea
+    dev = torch.device("cuda:0")
+    rows = []
+    for name, B, H, H_kv, n_q, n_k, d, dtype, backward in SPLIT_CASES:
+        t = inputgen.draw_gqa(B, H, H_kv, n_q, n_k, d, dtype, seed=2000 + len(rows), with_do=backward)
+        q, k, v = (t[x].to(dev) for x in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        m = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        l = torch.empty_like(m)
+        dt = mea.DTYPE_BF16 if dtype == "bf16" else mea.DTYPE_F32
+        splits = mea.attn_fwd_splitkv_num_splits(dt, B, H, H_kv, n_q, n_k, d, 0)
+        ws = torch.empty(max(16, mea.attn_fwd_splitkv_workspace_bytes(dt, B, H, H_kv, n_q, n_k, d, 0)),
+                         dtype=torch.uint8, device=dev)
+
+        def timed(fn):
+            for _ in range(warmup):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize(dev)
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize(dev)
+            return e0.elapsed_time(e1) / steps
+
+        flops = 4.0 * B * H * n_q * n_k * d
+        esz = q.element_size()
+        hbm = (2 * B * H_kv * n_k * d + 2 * B * H * n_q * d) * esz + 8 * B * H * n_q
+        ms_ex = timed(lambda: mea.attn_fwd_ex(q, k, v, out=o, row_max=m, row_sum=l))
+        ms_sp = timed(lambda: mea.attn_fwd_splitkv(q, k, v, num_splits=0, out=o, row_max=m,
+                                                   row_sum=l, workspace=ws))
+        row = {"case": name, "B": B, "H": H, "H_kv": H_kv, "n_q": n_q, "n_k": n_k, "d": d,
+               "dtype": dtype, "splits": splits,
+               "fwd_ex_ms": ms_ex, "fwd_splitkv_ms": ms_sp,
+               "fwd_ex_tflops": flops / (ms_ex * 1e-3) / 1e12,
+               "fwd_splitkv_tflops": flops / (ms_sp * 1e-3) / 1e12,
+               "compulsory_hbm_bytes": hbm,
+               "fwd_splitkv_hbm_gbs": hbm / (ms_sp * 1e-3) / 1e9,
+               "split_workspace_bytes": ws.numel() if splits > 1 else 0}
+        if backward:
+            do = t["do"].to(dev)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            bws = torch.empty(mea.attn_bwd_ex_workspace_bytes(dt, B, H, H_kv, n_q, n_k, d),
+                              dtype=torch.uint8, device=dev)
+            bms = timed(lambda: mea.attn_bwd_ex(q, k, v, o, do, m, l, dq=dq, dk=dk, dv=dv,
+                                                workspace=bws))
+            row["bwd_ex_ms"] = bms
+            row["bwd_ex_tflops"] = 2.5 * flops / (bms * 1e-3) / 1e12
+        rows.append(row)
+        log(json.dumps(row))
+        del t, q, k, v, o, m, l, ws
+        torch.cuda.empty_cache()
+    return {"mode": "splitkv", "steps": steps, "warmup": warmup, "rows": rows}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=("bench", "traffic", "configs"), default="bench",
+    ap.add_argument("--mode", choices=("bench", "traffic", "configs", "splitkv"), default="bench",
                     help="traffic: one 256 MiB copy (counter calibration) and one step, "
                          "for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs; configs: time "
                          "the forward on all five workloads (and the backward where the "
-                         "workload trains), one JSON line with a row per workload")
+                         "workload trains), one JSON line with a row per workload; splitkv: "
+                         "unsplit vs split-key forward on small-grid and decoding shapes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the attention "
@@ -168,6 +248,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.mode == "configs":
         print(json.dumps(sweep_configs(args.steps, args.warmup)), flush=True)
+        return
+    if args.mode == "splitkv":
+        print(json.dumps(sweep_split(args.steps, args.warmup)), flush=True)
         return
     w = inputgen.WORKLOADS["c3_long_bf16"]
     t = inputgen.draw(w.B, w.H, w.n, w.d, w.dtype, seed=w.seed, with_do=True)

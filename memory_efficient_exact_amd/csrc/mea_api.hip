@@ -18,10 +18,11 @@ constexpr int64_t kMaxN = int64_t(1) << 24;
 constexpr int64_t kMaxBH = int64_t(1) << 24;
 constexpr int64_t kMaxBlocks = int64_t(1) << 23;
 // Split-key planning: at most this many key ranges per head; the automatic
-// choice aims at this many workgroups (four per compute unit) and keeps at
-// least two key tiles in every range.
+// choice splits only grids of fewer than this many workgroups (two per
+// compute unit, what the forward kernels keep resident) and keeps at least
+// two key tiles in every range.
 constexpr int64_t kMaxSplits = 256;
-constexpr int64_t kAutoWorkgroups = 1024;
+constexpr int64_t kAutoWorkgroups = 512;
 constexpr int64_t kAutoMinTiles = 2;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -19,8 +19,11 @@
 //    (m_s - M) * log2(e)/sqrt(d) is formed in fp64 and rounded once, as in the
 //    kernel's own rescale; m = M / sqrt(d), l = L.
 //
-// HBM-bound: each row reads S * (d + 4) floats and writes d outputs. D/4 lanes
-// per row, 16 bytes each, so a wave reads whole rows of every partial.
+// HBM-bound in bytes (each row reads S * (d + 4) floats and writes d
+// outputs), latency-bound in practice when a few rows carry many ranges
+// (decoding). So a row is spread over CL = D/4 column lanes (16 bytes each)
+// times SL split lanes; split lane j takes ranges j, j + SL, ... and the SL
+// partial results of a row are combined through LDS.
 #include "mea_device.h"
 #include "mea_launch.h"
 
@@ -43,59 +46,107 @@ struct MergeArgs {
   double scale64;
 };
 
-template <int D, bool kBf16>
+template <int D, bool kBf16, int SL>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeArgs a) {
-  constexpr int LPR = D / 4;  // lanes per row
-  const int64_t gtid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t row = gtid / LPR;
-  const int col = (int)(gtid - row * LPR) * 4;
-  if (row >= a.rows) return;  // no barriers below
+  constexpr int CL = D / 4;        // column lanes per row
+  constexpr int TPR = CL * SL;     // threads per row
+  constexpr int RPW = kThreads / TPR;
+  static_assert(RPW * TPR == kThreads, "rows must tile the workgroup");
+  __shared__ double s_ref[RPW][SL];   // per split lane: max reference (R or fp64 m)
+  __shared__ float s_raw[RPW][SL];    // bf16: max raw score
+  __shared__ f32x4 s_acc[RPW][SL][CL];
+  __shared__ float s_sum[RPW][SL];
+
+  const int t = threadIdx.x;
+  const int rl = t / TPR;
+  const int j = (t - rl * TPR) / CL;
+  const int c = t - rl * TPR - j * CL;
+  const int64_t row = (int64_t)blockIdx.x * RPW + rl;
+  const bool live = row < a.rows;  // every thread reaches both barriers
 
   const float* rec0 = a.Ps + row * 4;
   const int64_t rstride = a.rows * 4;
-  const float* po0 = a.Po + row * D + col;
+  const float* po0 = a.Po + row * D + c * 4;
   const int64_t pstride = a.rows * D;
 
+  // 1. largest reference (and, for bf16, largest raw score) over this lane's ranges
+  double ref = -INFINITY;
+  float raw = -INFINITY;
+  if (live) {
+    for (int s = j; s < a.splits; s += SL) {
+      const float* r = rec0 + s * rstride;
+      if constexpr (kBf16) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(r);
+        raw = fmaxf(raw, v[0]);
+        ref = fmax(ref, (double)v[1]);
+      } else {
+        ref = fmax(ref, *reinterpret_cast<const double*>(r));
+      }
+    }
+  }
+  if (c == 0) {
+    s_ref[rl][j] = ref;
+    s_raw[rl][j] = raw;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < SL; ++i) {
+    ref = fmax(ref, s_ref[rl][i]);
+    raw = fmaxf(raw, s_raw[rl][i]);
+  }
+
+  // 2. this lane's ranges, re-based on the common reference
   f32x4 acc = f32x4{};
   float L = 0.f;
-  if constexpr (kBf16) {
-    float m_raw = -INFINITY, M = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) {
-      const f32x4 r = *reinterpret_cast<const f32x4*>(rec0 + s * rstride);
-      m_raw = fmaxf(m_raw, r[0]);
-      M = fmaxf(M, r[1]);
-    }
-    for (int s = 0; s < a.splits; ++s) {
-      const f32x4 r = *reinterpret_cast<const f32x4*>(rec0 + s * rstride);
-      const float w = r[2] * fast_exp2(r[1] - M);
+  if (live) {
+    const float refb = (float)ref;  // bf16: an fp32 value already
+    for (int s = j; s < a.splits; s += SL) {
+      const float* r = rec0 + s * rstride;
+      float w;
+      if constexpr (kBf16) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(r);
+        w = v[2] * fast_exp2(v[1] - refb);
+      } else {
+        w = r[2] * fast_exp2((float)((*reinterpret_cast<const double*>(r) - ref) * a.C64));
+      }
       L += w;
       acc += w * *reinterpret_cast<const f32x4*>(po0 + s * pstride);
     }
-    const float inv = 1.f / L;
+  }
+  s_acc[rl][j][c] = acc;
+  if (c == 0) s_sum[rl][j] = L;
+  __syncthreads();
+  if (!live || j != 0) return;
+#pragma unroll
+  for (int i = 1; i < SL; ++i) {
+    acc += s_acc[rl][i][c];
+    L += s_sum[rl][i];
+  }
+  const float inv = 1.f / L;
+  if constexpr (kBf16) {
     bf16x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = (bf16)(acc[e] * inv);
-    *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.O) + row * D + col) = o;
-    if (a.Mx != nullptr && col == 0) {
-      a.Mx[row] = m_raw * a.scale;
-      a.Ls[row] = L * fast_exp2(-__builtin_fmaf(m_raw, a.C, -M));
+    *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.O) + row * D + c * 4) = o;
+    if (a.Mx != nullptr && c == 0) {
+      a.Mx[row] = raw * a.scale;
+      a.Ls[row] = L * fast_exp2(-__builtin_fmaf(raw, a.C, -(float)ref));
     }
   } else {
-    double M = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) M = fmax(M, *reinterpret_cast<const double*>(rec0 + s * rstride));
-    for (int s = 0; s < a.splits; ++s) {
-      const float* r = rec0 + s * rstride;
-      const double m_s = *reinterpret_cast<const double*>(r);
-      const float w = r[2] * fast_exp2((float)((m_s - M) * a.C64));
-      L += w;
-      acc += w * *reinterpret_cast<const f32x4*>(po0 + s * pstride);
-    }
-    *reinterpret_cast<f32x4*>(static_cast<float*>(a.O) + row * D + col) = acc * (1.f / L);
-    if (a.Mx != nullptr && col == 0) {
-      a.Mx[row] = (float)(M * a.scale64);
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.O) + row * D + c * 4) = acc * inv;
+    if (a.Mx != nullptr && c == 0) {
+      a.Mx[row] = (float)(ref * a.scale64);
       a.Ls[row] = L;
     }
   }
+}
+
+template <int D, bool kBf16, int SL>
+hipError_t launch_sl(const MergeArgs& a, hipStream_t stream) {
+  constexpr int RPW = kThreads / (D / 4 * SL);
+  const int64_t blocks = (a.rows + RPW - 1) / RPW;
+  hipLaunchKernelGGL((merge_kernel<D, kBf16, SL>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 template <int D, bool kBf16>
@@ -112,10 +163,20 @@ hipError_t launch(const FwdProblem& p, hipStream_t stream) {
   a.C = kLog2e * a.scale;
   a.scale64 = 1.0 / sqrt((double)D);
   a.C64 = 1.4426950408889634 * a.scale64;
-  const int64_t threads = a.rows * (D / 4);
-  const int64_t blocks = (threads + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL((merge_kernel<D, kBf16>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  // more split lanes while there are ranges to share and the grid is small
+  constexpr int kMaxSL = kThreads / (D / 4);
+  int sl = 1;
+  while (sl * 2 <= kMaxSL && sl * 2 <= a.splits && a.rows * (D / 4) * sl < (int64_t)512 * kThreads)
+    sl *= 2;
+  switch (sl) {
+    case 1: return launch_sl<D, kBf16, 1>(a, stream);
+    case 2: return launch_sl<D, kBf16, 2>(a, stream);
+    case 4: return launch_sl<D, kBf16, 4>(a, stream);
+    case 8: return launch_sl<D, kBf16, 8>(a, stream);
+    default:
+      if constexpr (kMaxSL >= 16) return launch_sl<D, kBf16, 16>(a, stream);
+      return launch_sl<D, kBf16, 8>(a, stream);
+  }
 }
 
 }  // namespace
