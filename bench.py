@@ -87,7 +87,7 @@ def cpu_baseline(w):
 
 
 def sweep_configs(steps, warmup):
-    """Per workload: forward (and backward) time, TFLOP/s, peak extra device
+    """Per workload: forward and backward time, TFLOP/s, peak extra device
     memory beyond inputs and outputs, and the n^2 fp32 score-matrix size."""
     import torch
 
@@ -122,17 +122,20 @@ def sweep_configs(steps, warmup):
         fms = timed(lambda: mea.attn_fwd(q, k, v, out=o, row_max=m, row_sum=l))
         row["fwd_ms"] = fms
         row["fwd_tflops"] = w.fwd_flops() / (fms * 1e-3) / 1e12
-        if w.backward:
-            dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-            ws = torch.empty(mea.attn_bwd_workspace_bytes(mea.DTYPE_BF16, w.B, w.H, w.n, w.d),
-                             dtype=torch.uint8, device=dev)
-            before = torch.cuda.memory_allocated(dev)
-            torch.cuda.reset_peak_memory_stats(dev)
-            bms = timed(lambda: mea.attn_bwd(q, k, v, o, do, m, l, dq=dq, dk=dk, dv=dv, workspace=ws))
-            row["bwd_ms"] = bms
-            row["bwd_tflops"] = w.bwd_flops() / (bms * 1e-3) / 1e12
-            row["workspace_bytes"] = ws.numel()
-        row["peak_extra_bytes"] = torch.cuda.max_memory_allocated(dev) - before
+        row["fwd_peak_extra_bytes"] = torch.cuda.max_memory_allocated(dev) - before
+        # every workload also times the backward (the training workload is the one whose
+        # step includes it; for the others it is reported as extra information)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        dt = mea.DTYPE_BF16 if w.dtype == "bf16" else mea.DTYPE_F32
+        ws = torch.empty(mea.attn_bwd_workspace_bytes(dt, w.B, w.H, w.n, w.d),
+                         dtype=torch.uint8, device=dev)
+        before = torch.cuda.memory_allocated(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
+        bms = timed(lambda: mea.attn_bwd(q, k, v, o, do, m, l, dq=dq, dk=dk, dv=dv, workspace=ws))
+        row["bwd_ms"] = bms
+        row["bwd_tflops"] = w.bwd_flops() / (bms * 1e-3) / 1e12
+        row["workspace_bytes"] = ws.numel()
+        row["bwd_peak_extra_bytes"] = torch.cuda.max_memory_allocated(dev) - before
         row["stats_bytes"] = m.numel() * 8
         rows.append(row)
         log(json.dumps(row))

@@ -85,7 +85,10 @@ typedef enum {
  * q, k, v : inputs [B,H,n,d] in dt.            o : output [B,H,n,d] in dt.
  * row_max : output fp32 [B,H,n] or NULL: m_i = max_j q_i.k_j / sqrt(d)
  *           (natural units of the scaled score).
- * row_sum : output fp32 [B,H,n] or NULL: l_i = sum_j exp(q_i.k_j/sqrt(d) - m_i).
+ * row_sum : output fp32 [B,H,n] or NULL: l_i = sum_j exp(q_i.k_j/sqrt(d) - m_i)
+ *           for the m_i stored in row_max (for fp32 inputs the maximum is
+ *           found in fp64 and l_i re-based onto its fp32 rounding, so that
+ *           m_i + log(l_i) is the row's log-sum-exp to fp32 rounding of l_i).
  *           The two statistics are what attn_bwd needs; pass both or neither
  *           (passing exactly one is MEA_ERR_NULL).
  * No workspace: the only memory beyond inputs and outputs is the optional
@@ -96,9 +99,10 @@ MEA_API mea_status_t attn_fwd(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, i
                       float* row_max, float* row_sum, void* stream);
 
 /*
- * attn_bwd_workspace_bytes - bytes of device workspace attn_bwd needs:
- * 8*B*H*n (two fp32 values per query row: D_i = sum_c dO_ic * O_ic and the
- * base-2 log-sum-exp of the row). Returns 0 for empty or invalid shapes.
+ * attn_bwd_workspace_bytes - bytes of device workspace attn_bwd needs per
+ * query row, times B*H*n: 8 for bf16 (D_i = sum_c dO_ic * O_ic and the base-2
+ * log-sum-exp of the row, both fp32), 16 for fp32 (the log-sum-exp in fp64,
+ * D_i in fp32, padding). Returns 0 for empty or invalid shapes.
  */
 MEA_API size_t attn_bwd_workspace_bytes(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d);
 
@@ -121,8 +125,9 @@ MEA_API size_t attn_bwd_workspace_bytes(mea_dtype_t dt, int64_t B, int64_t H, in
  * workspace  : device scratch of at least attn_bwd_workspace_bytes(...) bytes,
  *              16-byte aligned, owned by the caller; its contents on entry do
  *              not matter and on return are unspecified.
- * Supported: dt = MEA_DTYPE_BF16 with d in {64, 128}. Other combinations
- * return MEA_ERR_UNSUPPORTED.
+ * Supported: dt in {MEA_DTYPE_BF16, MEA_DTYPE_F32} with d in {64, 128}. fp32
+ * inputs form scores on fp64 MFMA and the exponent in fp64, as the forward
+ * does; everything else is fp32.
  */
 MEA_API mea_status_t attn_bwd(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d,
                       const void* q, const void* k, const void* v, const void* o,
@@ -153,7 +158,8 @@ MEA_API mea_status_t attn_fwd_ex(mea_dtype_t dt, int64_t B, int64_t H, int64_t H
                          void* o, float* row_max, float* row_sum, void* stream);
 
 /*
- * attn_bwd_ex_workspace_bytes - workspace attn_bwd_ex needs: 8*B*H*n_q.
+ * attn_bwd_ex_workspace_bytes - workspace attn_bwd_ex needs: 8*B*H*n_q
+ * (bf16) or 16*B*H*n_q (fp32).
  * Returns 0 for empty or invalid shapes.
  */
 MEA_API size_t attn_bwd_ex_workspace_bytes(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv,
@@ -168,7 +174,7 @@ MEA_API size_t attn_bwd_ex_workspace_bytes(mea_dtype_t dt, int64_t B, int64_t H,
  * row_max, row_sum : the [B,H,n_q] statistics attn_fwd_ex wrote.
  * n_q = 0 with n_k > 0 writes dk = dv = 0 (only k, v, dk, dv are then
  * checked and the workspace may be NULL); n_k = 0 with n_q > 0 is
- * MEA_ERR_SHAPE. Supported: dt = MEA_DTYPE_BF16, d in {64, 128}.
+ * MEA_ERR_SHAPE. Supported: bf16 and fp32, d in {64, 128}.
  */
 MEA_API mea_status_t attn_bwd_ex(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_t n_q,
                          int64_t n_k, int64_t d, const void* q, const void* k, const void* v,

@@ -1,0 +1,378 @@
+// Backward attention for fp32 inputs on gfx950, by recomputation, with scores
+// formed in fp64.
+//
+// Method and formulas as in the bf16 backward (bwd_bf16.hip): the forward
+// keeps two numbers per query row, the probability tiles are rebuilt from
+// them ("Self-attention Does Not Need O(n^2) Memory": abstract; 方法详解;
+// English digest method bullets), and the gradients are the textbook softmax
+// Jacobian: dV = P^T dO, dP = dO V^T, D_i = dO_i . O_i, dS = P * (dP - D),
+// dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d).
+//
+// Precision (the 1e-5 bar of fp32 inputs). As in the fp32 forward, an fp32
+// product is exact in fp64, so S runs on fp64 MFMA (16x16x4) and the exponent
+// x * log2(e)/sqrt(d) - lse2 is formed in fp64 (at scores of ~1e4 an fp32
+// exponent would carry errors of ~1e-3). dP also runs on fp64 MFMA and D is
+// kept in fp64: dP - D cancels wherever P is concentrated (with a single key
+// it is exactly 0), and in fp32 the residue of that cancellation, summed over
+// many query rows into dK, reaches the tolerance. The weights, dS and the
+// three gradient products are fp32 (fp32 MFMA 16x16x4). lse2 = m*log2(e) +
+// log2(l) is formed per row in fp64 from the forward's statistics; the fp32
+// forward reports l relative to its reported (rounded) m, so the pair
+// reproduces the row's log-sum-exp to fp32 rounding of l alone.
+//
+// Two launches on the caller's stream:
+//  1. bwd_rows_f32: per query row {lse2, -D} (both fp64) into the workspace.
+//  2. bwd_main_f32: dK/dV workgroups (64 keys, 16 per wave, K and V of the
+//     wave's keys in registers) sweeping 32-row query tiles of Q, dO and the
+//     row terms staged in LDS; then dQ workgroups (64 queries, Q and dO in
+//     registers) sweeping 32-key tiles of K, V. Every output element is
+//     written once by one workgroup.
+//
+// Lane layouts (mea_device.h): S and dP (fp64 products) leave lane l,
+// register r at row 4r + l/16 of a 16-row block and column l%16; that
+// register is exactly the B operand lane l supplies for k-step r of the fp32
+// gradient products, whose k-step r covers rows 4r .. 4r + 3.
+#include "mea_device.h"
+#include "mea_launch.h"
+
+namespace mea {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 16 * kWaves;  // keys per dK/dV workgroup = queries per dQ workgroup
+constexpr int kTile = 32;           // staged rows per tile (two 16-row blocks)
+
+// per query row: lse2 = m*log2(e) + log2(l) and -D, both fp64; 16 bytes
+struct RowTerm {
+  double lse2;
+  double neg_d;
+};
+static_assert(sizeof(RowTerm) == 16, "row term layout");
+
+// ------------------------------------------------------------ 1. row terms
+// One thread per (row, 4 columns); the D/4 threads of a row reduce by shuffles.
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_rows_f32_kernel(
+    const float* __restrict__ O, const float* __restrict__ dO, const float* __restrict__ Mx,
+    const float* __restrict__ Ls, RowTerm* __restrict__ terms, int64_t rows) {
+  constexpr int LPR = D / 4;
+  const int64_t gtid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t row = gtid / LPR;
+  const int part = (int)(gtid - row * LPR);
+  double acc = 0.0;
+  if (row < rows) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(O + row * D + part * 4);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(dO + row * D + part * 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_fma((double)a[e], (double)b[e], acc);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < rows && part == 0) {
+    RowTerm t;
+    t.lse2 = (double)Mx[row] * 1.4426950408889634 + log2((double)Ls[row]);
+    t.neg_d = -acc;
+    terms[row] = t;
+  }
+}
+
+// ------------------------------------------------------------ 2. main kernel
+struct BwdArgs32 {
+  const float* Q;   // [heads, n_q, D]
+  const float* K;   // [heads, n_k, D]
+  const float* V;
+  const float* dO;  // [heads, n_q, D]
+  const RowTerm* T; // [heads, n_q]
+  float* dQ;
+  float* dK;
+  float* dV;
+  int n_q;
+  int n_k;
+  int tiles_kv;  // dK/dV workgroups per head
+  int tiles_q;   // dQ workgroups per head
+  int total_kv;
+  int total_q;
+  double C64;    // log2(e) / sqrt(D)
+  float scale;   // 1 / sqrt(D)
+};
+
+template <int D>
+struct Shared32 {
+  static constexpr int kStride = D + 4;          // row stride (floats): 16-byte pad
+  static constexpr int kElems = kTile * kStride;  // floats per staged tile
+  static constexpr int kLoads = kTile * D / 4 / kThreads;  // 16-byte loads per thread per tile
+  static_assert(kLoads * 4 * kThreads == kTile * D, "tile split");
+};
+
+// Register-staged copy of a kTile x D fp32 tile (rows past `rows` read as 0).
+template <int D>
+struct Stage {
+  u32x4 r[Shared32<D>::kLoads];
+  __device__ __forceinline__ void load(const float* src, int row0, int rows, int tid) {
+    constexpr int kCPR = D / 4;
+#pragma unroll
+    for (int i = 0; i < Shared32<D>::kLoads; ++i) {
+      const int c = tid + i * kThreads;
+      const int rr = c / kCPR;
+      const int ch = c - rr * kCPR;
+      r[i] = row0 + rr < rows ? *reinterpret_cast<const u32x4*>(src + (int64_t)(row0 + rr) * D + ch * 4)
+                              : u32x4{};
+    }
+  }
+  __device__ __forceinline__ void store(float* dst, int tid) const {
+    constexpr int kCPR = D / 4;
+#pragma unroll
+    for (int i = 0; i < Shared32<D>::kLoads; ++i) {
+      const int c = tid + i * kThreads;
+      const int rr = c / kCPR;
+      const int ch = c - rr * kCPR;
+      *reinterpret_cast<u32x4*>(dst + rr * Shared32<D>::kStride + ch * 4) = r[i];
+    }
+  }
+};
+
+// --- dK / dV role -------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void dkdv_role32(const BwdArgs32& a, int wg, float* sQ, float* sO,
+                                            RowTerm* sT) {
+  constexpr int S = Shared32<D>::kStride;
+  constexpr int E = Shared32<D>::kElems;
+  constexpr int KK = D / 4;   // k-steps over the head dimension
+  constexpr int CB = D / 16;  // 16-column output blocks
+  const int n_q = a.n_q, n_k = a.n_k;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int tile = xcd_remap(wg, a.total_kv);
+  const int bh = tile / a.tiles_kv;
+  const int kt = tile - bh * a.tiles_kv;
+  const float* Qh = a.Q + (int64_t)bh * n_q * D;
+  const float* dOh = a.dO + (int64_t)bh * n_q * D;
+  const RowTerm* Th = a.T + (int64_t)bh * n_q;
+  const int64_t kbase = (int64_t)bh * n_k * D;
+  const int key = kt * kRows + wave * 16 + l16;  // this lane's key (column of S)
+  const int krow = min(key, n_k - 1);
+
+  // B operands (fp64): K^T for S = Q K^T, V^T for dP = dO V^T
+  double kd[KK], vd[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    kd[kk] = (double)a.K[kbase + (int64_t)krow * D + 4 * kk + g4];
+    vd[kk] = (double)a.V[kbase + (int64_t)krow * D + 4 * kk + g4];
+  }
+  f32x4 accV[CB], accK[CB];  // dV^T, dK^T: register r <-> column 16*cb + 4*g4 + r
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    accV[cb] = f32x4{};
+    accK[cb] = f32x4{};
+  }
+
+  const int ntiles = (n_q + kTile - 1) / kTile;
+  Stage<D> stQ, stO;
+  RowTerm stT;
+  auto gload = [&](int i0) {
+    stQ.load(Qh, i0, n_q, tid);
+    stO.load(dOh, i0, n_q, tid);
+    if (tid < kTile) stT = i0 + tid < n_q ? Th[i0 + tid] : RowTerm{0.0, 0.0};
+  };
+  auto swrite = [&](int buf) {
+    stQ.store(sQ + buf * E, tid);
+    stO.store(sO + buf * E, tid);
+    if (tid < kTile) sT[buf * kTile + tid] = stT;
+  };
+  if (ntiles > 0) {  // no query rows at all: dK = dV = 0
+    gload(0);
+    swrite(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const int i0 = t * kTile;
+    if (t + 1 < ntiles) gload(i0 + kTile);
+    const float* qs = sQ + buf * E;
+    const float* os = sO + buf * E;
+    const RowTerm* ts = sT + buf * kTile;
+#pragma unroll
+    for (int qb = 0; qb < kTile / 16; ++qb) {
+      // S[q][key] and dP[q][key] (fp64): lane holds key l16, register r <-> query 16qb + 4r + g4
+      f64x4 s = f64x4{}, dp = f64x4{};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int off = (16 * qb + l16) * S + 4 * kk + g4;
+        s = mfma_f64_16x16x4((double)qs[off], kd[kk], s);
+        dp = mfma_f64_16x16x4((double)os[off], vd[kk], dp);
+      }
+      float p[4], ds[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int q = 16 * qb + 4 * r + g4;
+        const RowTerm rt = ts[q];
+        p[r] = fast_exp2((float)(s[r] * a.C64 - rt.lse2));
+        if (i0 + q >= n_q) p[r] = 0.f;  // padding query rows
+        ds[r] = p[r] * (float)(dp[r] + rt.neg_d);
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS: k-step r covers queries 16qb + 4r .. + 3
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int q = 16 * qb + 4 * r + g4;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          accV[cb] = mfma_f32_16x16x4(os[q * S + 16 * cb + l16], p[r], accV[cb]);
+          accK[cb] = mfma_f32_16x16x4(qs[q * S + 16 * cb + l16], ds[r], accK[cb]);
+        }
+      }
+    }
+    if (t + 1 < ntiles) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (key < n_k) {
+    float* vrow = a.dV + kbase + (int64_t)key * D;
+    float* krow_out = a.dK + kbase + (int64_t)key * D;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      *reinterpret_cast<f32x4*>(vrow + 16 * cb + 4 * g4) = accV[cb];
+      *reinterpret_cast<f32x4*>(krow_out + 16 * cb + 4 * g4) = accK[cb] * a.scale;
+    }
+  }
+}
+
+// --- dQ role --------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void dq_role32(const BwdArgs32& a, int wg, float* sK, float* sV) {
+  constexpr int S = Shared32<D>::kStride;
+  constexpr int E = Shared32<D>::kElems;
+  constexpr int KK = D / 4;
+  constexpr int CB = D / 16;
+  const int n_q = a.n_q, n_k = a.n_k;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int tile = xcd_remap(wg, a.total_q);
+  const int bh = tile / a.tiles_q;
+  const int qt = tile - bh * a.tiles_q;
+  const int64_t qbase = (int64_t)bh * n_q * D;
+  const float* Kh = a.K + (int64_t)bh * n_k * D;
+  const float* Vh = a.V + (int64_t)bh * n_k * D;
+  const int row = qt * kRows + wave * 16 + l16;  // this lane's query
+  const int qrow = min(row, n_q - 1);
+
+  // B operands (fp64): Q^T for S^T = K Q^T, dO^T for dP^T = V dO^T
+  double qd[KK], od[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    qd[kk] = (double)a.Q[qbase + (int64_t)qrow * D + 4 * kk + g4];
+    od[kk] = (double)a.dO[qbase + (int64_t)qrow * D + 4 * kk + g4];
+  }
+  const RowTerm rt = a.T[(int64_t)bh * n_q + qrow];
+  f32x4 acc[CB];  // dQ^T: register r <-> column 16*cb + 4*g4 + r
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x4{};
+
+  const int ntiles = (n_k + kTile - 1) / kTile;
+  Stage<D> stK, stV;
+  auto gload = [&](int j0) {
+    stK.load(Kh, j0, n_k, tid);
+    stV.load(Vh, j0, n_k, tid);
+  };
+  auto swrite = [&](int buf) {
+    stK.store(sK + buf * E, tid);
+    stV.store(sV + buf * E, tid);
+  };
+  gload(0);
+  swrite(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const int j0 = t * kTile;
+    if (t + 1 < ntiles) gload(j0 + kTile);
+    const float* ks = sK + buf * E;
+    const float* vs = sV + buf * E;
+#pragma unroll
+    for (int kb = 0; kb < kTile / 16; ++kb) {
+      // S^T[key][q] and dP^T (fp64): lane holds query l16, register r <-> key 16kb + 4r + g4
+      f64x4 s = f64x4{}, dp = f64x4{};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int off = (16 * kb + l16) * S + 4 * kk + g4;
+        s = mfma_f64_16x16x4((double)ks[off], qd[kk], s);
+        dp = mfma_f64_16x16x4((double)vs[off], od[kk], dp);
+      }
+      float ds[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float p = fast_exp2((float)(s[r] * a.C64 - rt.lse2));
+        if (j0 + 16 * kb + 4 * r + g4 >= n_k) p = 0.f;  // padding keys
+        ds[r] = p * (float)(dp[r] + rt.neg_d);
+      }
+      // dQ^T += K^T dS^T: k-step r covers keys 16kb + 4r .. + 3
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kr = 16 * kb + 4 * r + g4;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) acc[cb] = mfma_f32_16x16x4(ks[kr * S + 16 * cb + l16], ds[r], acc[cb]);
+      }
+    }
+    if (t + 1 < ntiles) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (row < n_q) {
+    float* qout = a.dQ + qbase + (int64_t)row * D;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      *reinterpret_cast<f32x4*>(qout + 16 * cb + 4 * g4) = acc[cb] * a.scale;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_main_f32_kernel(const BwdArgs32 a) {
+  __shared__ __attribute__((aligned(16))) float s0[2 * Shared32<D>::kElems];
+  __shared__ __attribute__((aligned(16))) float s1[2 * Shared32<D>::kElems];
+  __shared__ __attribute__((aligned(16))) RowTerm sT[2 * kTile];
+  const int wg = blockIdx.x;
+  if (wg < a.total_kv) dkdv_role32<D>(a, wg, s0, s1, sT);
+  else dq_role32<D>(a, wg - a.total_kv, s0, s1);
+}
+
+template <int D>
+hipError_t launch(const BwdProblem& p, hipStream_t stream) {
+  const int64_t rows = p.heads * p.rows_q;
+  RowTerm* terms = reinterpret_cast<RowTerm*>(p.ws);
+  if (rows > 0) {
+    const int64_t threads = rows * (D / 4);
+    const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL((bwd_rows_f32_kernel<D>), dim3(blocks), dim3(kThreads), 0, stream,
+                       (const float*)p.o, (const float*)p.dO, p.m, p.l, terms, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  BwdArgs32 a;
+  a.Q = (const float*)p.q;
+  a.K = (const float*)p.k;
+  a.V = (const float*)p.v;
+  a.dO = (const float*)p.dO;
+  a.T = terms;
+  a.dQ = (float*)p.dq;
+  a.dK = (float*)p.dk;
+  a.dV = (float*)p.dv;
+  a.n_q = p.rows_q;
+  a.n_k = p.n_k;
+  a.tiles_kv = (p.n_k + kRows - 1) / kRows;
+  a.tiles_q = (p.rows_q + kRows - 1) / kRows;
+  a.total_kv = (int)(p.heads * a.tiles_kv);
+  a.total_q = (int)(p.heads * a.tiles_q);
+  a.scale = 1.0f / sqrtf((float)D);
+  a.C64 = 1.4426950408889634 / sqrt((double)D);
+  hipLaunchKernelGGL((bwd_main_f32_kernel<D>), dim3((unsigned)(a.total_kv + a.total_q)),
+                     dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_f32(int d, const BwdProblem& p, hipStream_t stream) {
+  if (d == 64) return launch<64>(p, stream);
+  return launch<128>(p, stream);
+}
+
+}  // namespace mea

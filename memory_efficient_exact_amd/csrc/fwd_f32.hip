@@ -218,8 +218,12 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs32 a) {
         rec[2] = l_tot;
         rec[3] = 0.f;
       } else if (a.Mx != nullptr) {
-        a.Mx[grow] = (float)(m_run * a.scale64);
-        a.Ls[grow] = l_tot;
+        // report l against the reported (fp32-rounded) maximum, so that the pair
+        // satisfies l = sum_j exp(s_j - m) as stored: l_tot * exp(m - fl(m))
+        const double m_nat = m_run * a.scale64;
+        const float m_st = (float)m_nat;
+        a.Mx[grow] = m_st;
+        a.Ls[grow] = (float)((double)l_tot * exp(m_nat - (double)m_st));
       }
     }
   }

@@ -63,6 +63,10 @@ mea_status_t check_shape(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int
   return MEA_OK;
 }
 
+// Backward workspace per query row: bf16 keeps {-D, lse2} as two floats; fp32
+// keeps lse2 in fp64 (scores of ~1e4 need more than fp32 there) and -D.
+size_t bwd_row_bytes(bool bf16) { return bf16 ? 8 : 16; }
+
 mea_status_t check_ptrs(std::initializer_list<const void*> ptrs) {
   for (const void* p : ptrs)
     if (p == nullptr) return MEA_ERR_NULL;
@@ -153,12 +157,11 @@ mea_status_t bwd_impl(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_
   mea_status_t st = check_shape(dt, B, H, H_kv, n_q, n_k, d, &s);
   if (st != MEA_OK || s.empty) return st;
   if (n_k == 0) return MEA_ERR_SHAPE;  // query rows without keys have no forward
-  if (dt != MEA_DTYPE_BF16) return MEA_ERR_UNSUPPORTED;
   // without query rows only the key side is touched (dk = dv = 0)
   st = s.rows_q > 0 ? check_ptrs({q, k, v, o, dO, row_max, row_sum, dq, dk, dv})
                     : check_ptrs({k, v, dk, dv});
   if (st != MEA_OK) return st;
-  const size_t need = (size_t)(8 * s.q_rows_total);
+  const size_t need = bwd_row_bytes(s.bf16) * (size_t)s.q_rows_total;
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return MEA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MEA_ERR_ALIGN;
@@ -178,7 +181,8 @@ mea_status_t bwd_impl(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_
   p.dk = dk;
   p.dv = dv;
   p.ws = static_cast<float*>(workspace);
-  hipError_t e = mea::launch_bwd_bf16(s.d, p, reinterpret_cast<hipStream_t>(stream));
+  hipStream_t st_h = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = s.bf16 ? mea::launch_bwd_bf16(s.d, p, st_h) : mea::launch_bwd_f32(s.d, p, st_h);
   return e == hipSuccess ? MEA_OK : MEA_ERR_LAUNCH;
 }
 
@@ -186,7 +190,7 @@ size_t bwd_ws_bytes(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_t 
                     int64_t d) {
   Shape s;
   if (check_shape(dt, B, H, H_kv, n_q, n_k, d, &s) != MEA_OK || s.empty) return 0;
-  return (size_t)(8 * s.q_rows_total);
+  return bwd_row_bytes(s.bf16) * (size_t)s.q_rows_total;
 }
 
 }  // namespace

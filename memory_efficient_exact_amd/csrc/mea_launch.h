@@ -64,10 +64,12 @@ struct BwdProblem {
   void* dq = nullptr;
   void* dk = nullptr;  // [heads, n_k, d]: sums over the query heads of each group
   void* dv = nullptr;
-  float* ws = nullptr;  // 2 * heads * rows_q floats
+  float* ws = nullptr;  // row terms, bwd_workspace_per_row(dtype) bytes per query row
 };
 
-// bf16 backward: row preprocess, then one grid with dK/dV and dQ workgroups.
+// Backward: row preprocess, then one grid with dK/dV and dQ workgroups.
+// bf16: ws holds 2 floats per query row; fp32: 16 bytes per query row.
 hipError_t launch_bwd_bf16(int d, const BwdProblem& p, hipStream_t stream);
+hipError_t launch_bwd_f32(int d, const BwdProblem& p, hipStream_t stream);
 
 }  // namespace mea

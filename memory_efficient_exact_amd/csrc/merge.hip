@@ -17,7 +17,7 @@
 //    unsplit kernel: m = (max_s m_s) / sqrt(d), l = L * 2^(M - m_raw * C).
 //  * fp32 inputs: record {m_s (fp64 raw max), l_s}; the exponent
 //    (m_s - M) * log2(e)/sqrt(d) is formed in fp64 and rounded once, as in the
-//    kernel's own rescale; m = M / sqrt(d), l = L.
+//    kernel's own rescale; m = fl(M / sqrt(d)), l = L * exp(M / sqrt(d) - m).
 //
 // HBM-bound in bytes (each row reads S * (d + 4) floats and writes d
 // outputs), latency-bound in practice when a few rows carry many ranges
@@ -135,8 +135,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeArgs a) {
   } else {
     *reinterpret_cast<f32x4*>(static_cast<float*>(a.O) + row * D + c * 4) = acc * inv;
     if (a.Mx != nullptr && c == 0) {
-      a.Mx[row] = (float)(ref * a.scale64);
-      a.Ls[row] = L;
+      // as in the unsplit kernel: l against the reported (rounded) maximum
+      const double m_nat = ref * a.scale64;
+      const float m_st = (float)m_nat;
+      a.Mx[row] = m_st;
+      a.Ls[row] = (float)((double)L * exp(m_nat - (double)m_st));
     }
   }
 }

@@ -102,7 +102,13 @@ def test_fwd_empty_is_noop(L):
 
 
 def test_bwd_validation(L):
-    assert bwd(L, dt=F32) == UNSUP
+    assert bwd(L, dt=2) == UNSUP
+    # fp32 keeps 16 bytes per query row (fp64 log-sum-exp); every call below stops
+    # in validation (a passing fp32 call would launch on the fake pointers)
+    assert bwd(L, dt=F32, wsb=16 * 128 - 1) == WS
+    assert bwd(L, dt=F32, ws=0) == WS
+    assert bwd(L, dt=F32, ptrs={"dq": 0}) == NULL
+    assert bwd(L, dt=F32, d=96) == UNSUP
     assert bwd(L, d=256) == UNSUP
     assert bwd(L, n=-5) == SHAPE
     for name in ("q", "k", "v", "o", "do", "m", "l", "dq", "dk", "dv"):
@@ -116,6 +122,7 @@ def test_bwd_validation(L):
 
 def test_workspace_bytes(L):
     assert mea.attn_bwd_workspace_bytes(BF16, 2, 8, 8192, 64) == 8 * 2 * 8 * 8192
+    assert mea.attn_bwd_workspace_bytes(F32, 2, 8, 8192, 128) == 16 * 2 * 8 * 8192
     assert mea.attn_bwd_workspace_bytes(BF16, 0, 8, 8192, 64) == 0
     assert mea.attn_bwd_workspace_bytes(BF16, 1, 1, 5, 96) == 0
     assert mea.attn_bwd_workspace_bytes(BF16, -1, 1, 5, 64) == 0
@@ -176,7 +183,8 @@ def test_fwd_ex_validation(L):
 
 
 def test_bwd_ex_validation(L):
-    assert bwd_ex(L, dt=F32) == UNSUP
+    assert bwd_ex(L, dt=5) == UNSUP
+    assert bwd_ex(L, dt=F32, wsb=16 * 4 * 16 - 1) == WS
     assert bwd_ex(L, H_kv=3) == SHAPE
     assert bwd_ex(L, n_k=0) == SHAPE
     for name in ("q", "k", "v", "o", "do", "m", "l", "dq", "dk", "dv"):

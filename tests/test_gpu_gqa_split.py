@@ -43,26 +43,28 @@ def test_fwd_ex_small_full(dtype, d, B, H, H_kv, n_q, n_k):
     check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, dtype)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("B,H,H_kv,n_q,n_k", [(1, 4, 2, 17, 300), (1, 8, 1, 33, 129),
                                               (2, 4, 4, 100, 37), (1, 2, 1, 1, 200),
                                               (1, 4, 2, 300, 1), (1, 6, 2, 130, 260)])
-def test_bwd_ex_small_full(d, B, H, H_kv, n_q, n_k):
-    say("bwd_ex", d, B, H, H_kv, n_q, n_k)
-    t = draw(B, H, H_kv, n_q, n_k, d, "bf16", seed=31 + n_q + n_k + d, with_do=True)
+def test_bwd_ex_small_full(dtype, d, B, H, H_kv, n_q, n_k):
+    say("bwd_ex", dtype, d, B, H, H_kv, n_q, n_k)
+    t = draw(B, H, H_kv, n_q, n_k, d, dtype, seed=31 + n_q + n_k + d, with_do=True)
     q, k, v, do = (gpu(t[x]) for x in ("q", "k", "v", "do"))
     o, m, l = mea.attn_fwd_ex(q, k, v)
     dq, dk, dv = mea.attn_bwd_ex(q, k, v, o, do, m, l)
     torch.cuda.synchronize()
     rq, rk, rv = oracle.gqa_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]))
-    check("dQ", f64(dq.cpu()), rq, "bf16")
-    check("dK", f64(dk.cpu()), rk, "bf16")
-    check("dV", f64(dv.cpu()), rv, "bf16")
+    check("dQ", f64(dq.cpu()), rq, dtype)
+    check("dK", f64(dk.cpu()), rk, dtype)
+    check("dV", f64(dv.cpu()), rv, dtype)
 
 
-def test_bwd_ex_without_queries_gives_zero_key_gradients():
-    say("bwd_ex n_q=0")
-    t = draw(1, 4, 2, 0, 200, 64, "bf16", seed=41, with_do=True)
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_bwd_ex_without_queries_gives_zero_key_gradients(dtype):
+    say("bwd_ex n_q=0", dtype)
+    t = draw(1, 4, 2, 0, 200, 64, dtype, seed=41, with_do=True)
     q, k, v, do = (gpu(t[x]) for x in ("q", "k", "v", "do"))
     o = torch.empty_like(q)
     m = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)

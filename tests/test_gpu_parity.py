@@ -75,11 +75,17 @@ def check(name, got, ref, dtype):
 
 
 def check_stats(m, l, m_ref, l_ref, dtype):
+    """Row statistics: m (natural units, fp32 rounding of a score of size |m|)
+    and the log-sum-exp m + log(l). The pair is stored so that l sums
+    exp(s - m) for the stored m; where m was rounded only l absorbs it, and
+    m + log(l) does not depend on the rounding (at scores of ~1e4 fp32
+    rounding of m alone moves l by 2e-4)."""
     m = np.asarray(m, np.float64)
     l = np.asarray(l, np.float64)
-    # m in natural units: fp32 rounding of a score of size |m|
     np.testing.assert_allclose(m, m_ref, rtol=2e-6, atol=1e-6)
-    np.testing.assert_allclose(l, l_ref, rtol=1e-4 if dtype == "bf16" else 1e-5, atol=0)
+    lse = m + np.log(l)
+    lse_ref = np.asarray(m_ref, np.float64) + np.log(np.asarray(l_ref, np.float64))
+    np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-4 if dtype == "bf16" else 1e-5)
 
 
 # ------------------------------------------------------------ small, full compare
@@ -100,19 +106,54 @@ def test_fwd_small_full(dtype, d, B, H, n):
     check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, dtype)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("B,H,n", [(1, 1, 1), (1, 1, 17), (1, 3, 130), (2, 1, 300), (1, 1, 256)])
-def test_bwd_small_full(d, B, H, n):
-    say("bwd small", d, B, H, n)
-    t = inputgen.draw(B, H, n, d, "bf16", seed=11 + n + d, with_do=True)
+def test_bwd_small_full(dtype, d, B, H, n):
+    say("bwd small", dtype, d, B, H, n)
+    t = inputgen.draw(B, H, n, d, dtype, seed=11 + n + d, with_do=True)
     q, k, v, do = (gpu(t[x]) for x in ("q", "k", "v", "do"))
     o, m, l = mea.attn_fwd(q, k, v)
     dq, dk, dv = mea.attn_bwd(q, k, v, o, do, m, l)
     torch.cuda.synchronize()
     rq, rk, rv = oracle.naive_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]))
-    check("dQ", f64(dq.cpu()), rq, "bf16")
-    check("dK", f64(dk.cpu()), rk, "bf16")
-    check("dV", f64(dv.cpu()), rv, "bf16")
+    check("dQ", f64(dq.cpu()), rq, dtype)
+    check("dK", f64(dk.cpu()), rk, dtype)
+    check("dV", f64(dv.cpu()), rv, dtype)
+
+
+def test_bwd_fp32_single_head_workload_full():
+    # the 1 x 1 x 1024 x 64 fp32 workload, forward then backward, every element
+    w = inputgen.WORKLOADS["c1_single_head_fp32"]
+    say("bwd fp32", w.name)
+    t = inputgen.make_inputs(w, with_do=True)
+    q, k, v, do = (gpu(t[x]) for x in ("q", "k", "v", "do"))
+    o, m, l = mea.attn_fwd(q, k, v)
+    dq, dk, dv = mea.attn_bwd(q, k, v, o, do, m, l)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.naive_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]))
+    check("dQ", f64(dq.cpu()), rq, "fp32")
+    check("dK", f64(dk.cpu()), rk, "fp32")
+    check("dV", f64(dv.cpu()), rv, "fp32")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_fp32_stress_scores(d):
+    # Q and K scaled by 30 (scaled scores in the hundreds to thousands) and one head of
+    # all-equal keys, as in the fp32 stress workload: the probabilities are rebuilt from
+    # the stored statistics, so their fp32 rounding must not leak into the gradients
+    say("bwd fp32 stress", d)
+    t = inputgen.draw(1, 2, 1500, d, "fp32", seed=17 + d, qk_scale=30.0, equal_key_heads=(0,),
+                      with_do=True)
+    q, k, v, do = (gpu(t[x]) for x in ("q", "k", "v", "do"))
+    o, m, l = mea.attn_fwd(q, k, v)
+    dq, dk, dv = mea.attn_bwd(q, k, v, o, do, m, l)
+    torch.cuda.synchronize()
+    assert float(m.abs().max()) > 300.0
+    rq, rk, rv = oracle.naive_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]))
+    check("dQ", f64(dq.cpu()), rq, "fp32")
+    check("dK", f64(dk.cpu()), rk, "fp32")
+    check("dV", f64(dv.cpu()), rv, "fp32")
 
 
 # ------------------------------------------------------------ invariants on GPU output
@@ -124,7 +165,15 @@ def test_n1_returns_v_bitwise(dtype, d):
     t = inputgen.draw(2, 3, 1, d, dtype, seed=3)
     o, m, l = run_fwd(t)
     assert torch.equal(o.cpu(), t["v"])
-    assert torch.all(l.cpu() == 1.0)
+    if dtype == "bf16":
+        assert torch.all(l.cpu() == 1.0)
+    else:
+        # fp32: m is the fp64 score rounded to fp32 and l = exp(s - m) absorbs that
+        # rounding, so m + log(l) is the score itself
+        s = (f64(t["q"]) * f64(t["k"])).sum(-1) / math.sqrt(d)
+        lse = m.cpu().double().numpy() + np.log(l.cpu().double().numpy())
+        np.testing.assert_allclose(lse, s, rtol=0, atol=1e-6)
+        assert np.all(np.abs(l.cpu().numpy() - 1.0) <= 2.0 ** -20)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
@@ -134,7 +183,14 @@ def test_identical_keys_give_mean_of_values(dtype):
     o, m, l = run_fwd(t)
     mean = f64(t["v"]).mean(axis=2, keepdims=True)
     check("O", f64(o.cpu()), np.broadcast_to(mean, o.shape), dtype)
-    np.testing.assert_allclose(l.cpu().numpy(), 333.0, rtol=1e-5)
+    if dtype == "bf16":
+        np.testing.assert_allclose(l.cpu().numpy(), 333.0, rtol=1e-5)
+    else:
+        # fp32 at scores of ~1e4: l is re-based onto the fp32-rounded maximum, so the
+        # log-sum-exp is what equals s + log(333)
+        s = (f64(t["q"]) * f64(t["k"])[:, :, :1, :]).sum(-1) / math.sqrt(128)
+        lse = m.cpu().double().numpy() + np.log(l.cpu().double().numpy())
+        np.testing.assert_allclose(lse, s + math.log(333.0), rtol=0, atol=1e-5)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
