@@ -32,6 +32,13 @@
 // block. The true running max m is tracked separately; the statistics are
 // reported for it: l = sum_j exp(s_j - m) = l_R * exp2(R - m*C).
 //
+// The common path of a block is cheap: each lane folds its 16 scores per
+// query block into its own running maximum and compares that with a
+// precomputed raw-score threshold (R + 8) / C; one wave-wide test covers all
+// query blocks. Only when it fires are the two lanes of a row combined
+// (v_permlane32_swap) to rebase on the row maximum; the exact row maximum for
+// the statistics is formed once, after the sweep.
+//
 // Key ranges. A workgroup may cover only the keys [key0, key0 + split_len) of its
 // head (split-key mode, for grids too small to fill the chip). It then writes
 // the summary of that range instead of the output: the normalised fp32 row
@@ -126,14 +133,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const FwdArgs a) 
     }
   }
 
-  float m_run[QB];  // running max of raw scores q.k (exact)
-  float ref[QB];    // reference R (see header)
-  float l_run[QB];  // this lane's share of sum_j exp2(x_j*C - R)
+  float m_lane[QB];  // running max of the raw scores q.k this lane holds (exact);
+                     // the row maximum is the max over the lane pair (l, l ^ 32)
+  float ref[QB];     // reference R (see header), the same in both lanes of a row
+  float thr[QB];     // raw-score threshold (R + slack) / C: a lane maximum above it
+                     // calls for a new reference
+  float l_run[QB];   // this lane's share of sum_j exp2(x_j*C - R)
   f32x16 acc[QB][DB];
+  const float invC = 1.0f / C;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
+    m_lane[qb] = -INFINITY;
     ref[qb] = -INFINITY;
+    thr[qb] = -INFINITY;
     l_run[qb] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
@@ -197,21 +209,30 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const FwdArgs a) 
     }
     // P^T fragments: chunk c (keys 16c..16c+15 of the block), element e is register 8c + e
     bf16x8 pf[QB][2];
+    // lane maxima; one wave-wide test for all query blocks (rarely true after the first block)
+    bool moved = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = fmaxf(s[qb][0], s[qb][1]);
+      float mx = m_lane[qb];
 #pragma unroll
-      for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[qb][r]);
-      mx = pair_max32(mx);
-      m_run[qb] = fmaxf(m_run[qb], mx);
-      const float target = m_run[qb] * C;
-      if (wave_any(target > ref[qb] + kRefSlack)) {
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][r]);
+      m_lane[qb] = mx;
+      moved |= mx > thr[qb];
+    }
+    if (wave_any(moved)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float target = pair_max32(m_lane[qb]) * C;  // row maximum, log2 units
         const float alpha = fast_exp2(ref[qb] - target);  // 0 on the first block
         ref[qb] = target;
+        thr[qb] = (target + kRefSlack) * invC;
         l_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
       }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
       const float R = ref[qb];
       float ls = 0.f;
 #pragma unroll
@@ -263,6 +284,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const FwdArgs a) 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = q0 + qb * 32 + l32;
+    const float m_row = pair_max32(m_lane[qb]);
     const float l_tot = pair_sum32(l_run[qb]);
     const float inv = 1.f / l_tot;
     if (row >= n_q) continue;
@@ -281,8 +303,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const FwdArgs a) 
       if (a.Mx != nullptr && hi == 0) {
         // l_tot sums exp2(x*C - R) = exp(s - m) * 2^(m*C - R); m*C - R is
         // formed exactly by one FMA
-        const float shift = __builtin_fmaf(m_run[qb], C, -ref[qb]);
-        a.Mx[grow] = m_run[qb] * a.scale;
+        const float shift = __builtin_fmaf(m_row, C, -ref[qb]);
+        a.Mx[grow] = m_row * a.scale;
         a.Ls[grow] = l_tot * fast_exp2(-shift);
       }
     } else {
@@ -298,7 +320,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const FwdArgs a) 
           for (int e = 0; e < 4; ++e) w[e] = acc[qb][db][4 * r4 + e] * inv;
           *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * r4 + 4 * hi) = w;
         }
-      if (hi == 0) *reinterpret_cast<f32x4*>(a.Ps + prow * 4) = f32x4{m_run[qb], ref[qb], l_tot, 0.f};
+      if (hi == 0) *reinterpret_cast<f32x4*>(a.Ps + prow * 4) = f32x4{m_row, ref[qb], l_tot, 0.f};
     }
   }
 }
