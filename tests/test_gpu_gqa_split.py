@@ -161,3 +161,55 @@ def test_splitkv_decode_step(dtype, d):
     check("O split", f64(o.cpu()), o_ref, dtype)
     check("O unsplit", f64(o1.cpu()), o_ref, dtype)
     check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, dtype)
+
+
+# ------------------------------------------------------- larger grouped-query shapes
+
+def test_gqa_prefill_sampled_rows_fwd_bwd():
+    # 32 query heads over 8 key/value heads, 2048 tokens, d = 128, forward and backward;
+    # sampled query rows for O and dQ, sampled key rows for dK and dV (the oracle forms
+    # every row's full softmax for them)
+    B, H, H_kv, n, d = 1, 32, 8, 2048, 128
+    say("gqa prefill", B, H, H_kv, n, d)
+    t = draw(B, H, H_kv, n, n, d, "bf16", seed=91, with_do=True)
+    q, k, v, do = (gpu(t[x]) for x in ("q", "k", "v", "do"))
+    o, m, l = mea.attn_fwd_ex(q, k, v)
+    dq, dk, dv = mea.attn_bwd_ex(q, k, v, o, do, m, l)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(92)
+    rows = np.concatenate([rng.choice(n, 30, replace=False), [0, n - 1]])
+    cols = np.concatenate([rng.choice(n, 30, replace=False), [0, n - 1]])
+    o_ref, m_ref, l_ref = oracle.gqa_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), rows=rows)
+    check("O", f64(o.cpu())[:, :, rows], o_ref, "bf16")
+    check_stats(m.cpu().numpy()[:, :, rows], l.cpu().numpy()[:, :, rows], m_ref, l_ref, "bf16")
+    rq, rk, rv = oracle.gqa_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]), rows=rows,
+                                cols=cols)
+    check("dQ", f64(dq.cpu())[:, :, rows], rq, "bf16")
+    check("dK", f64(dk.cpu())[:, :, cols], rk, "bf16")
+    check("dV", f64(dv.cpu())[:, :, cols], rv, "bf16")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 64)])
+def test_multi_token_decode_split(dtype, d):
+    # 4 new queries per head (32 heads over 8 key/value heads) against a 32768-entry cache
+    B, H, H_kv, n_q, n_k = 2, 32, 8, 4, 32768
+    say("decode 4 tokens", dtype, d)
+    t = draw(B, H, H_kv, n_q, n_k, d, dtype, seed=93)
+    o, m, l = mea.attn_fwd_splitkv(gpu(t["q"]), gpu(t["k"]), gpu(t["v"]))
+    torch.cuda.synchronize()
+    o_ref, m_ref, l_ref = oracle.gqa_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]))
+    check("O", f64(o.cpu()), o_ref, dtype)
+    check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, dtype)
+
+
+def test_splitkv_bf16_large_scores():
+    # bf16 inputs with Q and K scaled by 30: range maxima far apart, every range re-based
+    say("splitkv bf16 x30")
+    t = draw(1, 4, 2, 200, 3000, 64, "bf16", seed=94, qk_scale=30.0)
+    o, m, l = mea.attn_fwd_splitkv(gpu(t["q"]), gpu(t["k"]), gpu(t["v"]), num_splits=12)
+    o1, m1, l1 = mea.attn_fwd_ex(gpu(t["q"]), gpu(t["k"]), gpu(t["v"]))
+    torch.cuda.synchronize()
+    o_ref, m_ref, l_ref = oracle.gqa_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]))
+    check("O split", f64(o.cpu()), o_ref, "bf16")
+    check("O unsplit", f64(o1.cpu()), o_ref, "bf16")
+    check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, "bf16")
