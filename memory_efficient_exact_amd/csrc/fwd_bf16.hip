@@ -39,6 +39,13 @@
 // (v_permlane32_swap) to rebase on the row maximum; the exact row maximum for
 // the statistics is formed once, after the sweep.
 //
+// Decoding mode (few query rows per head, e.g. one new token per query head of
+// a group): the four waves share one 32-row query block and take different
+// 32-key blocks of every 128-key tile, so no MFMA or VALU work is spent on
+// padding query rows. After the sweep the waves' partial results (maximum,
+// reference, sum, accumulator) are merged through LDS with the same re-basing
+// rule, and each wave writes a quarter of the output columns.
+//
 // Key ranges. A workgroup may cover only the keys [key0, key0 + split_len) of its
 // head (split-key mode, for grids too small to fill the chip). It then writes
 // the summary of that range instead of the output: the normalised fp32 row
@@ -77,9 +84,12 @@ struct FwdArgs {
   float scale;    // 1 / sqrt(D)
 };
 
-template <int D, int QB, int BC>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const FwdArgs a) {
-  constexpr int kBQ = kWaves * QB * 32;  // query rows per workgroup
+// two workgroups per CU, except decoding at d = 128, whose 128-key tiles
+// (139 KiB of LDS double-buffered) leave room for one
+template <int D, int QB, int BC, bool kDecode>
+__global__ __launch_bounds__(kThreads, (kDecode && D == 128) ? 1 : 2) void fwd_bf16_kernel(const FwdArgs a) {
+  static_assert(!kDecode || (QB == 1 && BC == 32 * kWaves), "decoding: one 32-key block per wave");
+  constexpr int kBQ = kDecode ? 32 : kWaves * QB * 32;  // query rows per workgroup
   constexpr int DK = D / 16;             // k-steps of the score MFMA
   constexpr int DB = D / 32;             // 32-wide output column blocks
   constexpr int SB = BC / 32;            // 32-key blocks per LDS tile
@@ -119,7 +129,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const FwdArgs a) 
   const bf16* Qh = a.Q + (int64_t)bh * n_q * D;
   const bf16* Kh = a.K + ((int64_t)bh * a.n_k + key0) * D;
   const bf16* Vh = a.V + ((int64_t)bh * a.n_k + key0) * D;
-  const int q0 = qt * kBQ + wave * QB * 32;
+  const int q0 = kDecode ? qt * kBQ : qt * kBQ + wave * QB * 32;
 
   // Q fragments: B operand of S^T = K Q^T (lane: query l32, 8 columns at 16*dk + 8*hi)
   bf16x8 qf[QB][DK];
@@ -260,7 +270,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const FwdArgs a) 
   auto step = [&](const bf16* ks, const bf16* vs, bf16* kn, bf16* vn, int t) {
     const int j0 = t * BC;
     if (t + 1 < ntiles) issue(kn, vn, j0 + BC);
-    if (j0 + BC <= n) {
+    if constexpr (kDecode) {  // this wave's 32-key block of the tile
+      if (j0 + BC <= n) block(ks, vs, wave, j0, std::false_type{});
+      else if (j0 + wave * 32 < n) block(ks, vs, wave, j0, std::true_type{});
+    } else if (j0 + BC <= n) {
 #pragma unroll 1
       for (int sb = 0; sb < SB; ++sb) block(ks, vs, sb, j0, std::false_type{});
     } else {  // ragged last tile
@@ -278,6 +291,83 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const FwdArgs a) 
   for (int t = 0; t < ntiles; t += 2) {
     step(sK0, sV0, sK1, sV1, t);
     if (t + 1 < ntiles) step(sK1, sV1, sK0, sV0, t + 1);
+  }
+
+  if constexpr (kDecode) {
+    // Merge the four waves' partial results (same 32 query rows, different
+    // keys). The last step ended with a barrier and no DMA in flight, so the
+    // tile buffers are free: per-wave statistics go to sV0, each wave's
+    // re-based accumulator (32 rows x D fp32, rows padded) to sK0 / sK1.
+    constexpr int AS = D + 4;
+    float* st = reinterpret_cast<float*>(sV0);  // [3][kWaves][32]: R, row max, row sum
+    float* sacc = reinterpret_cast<float*>(wave < 2 ? sK0 : sK1) + (wave & 1) * 32 * AS;
+    static_assert(2 * 32 * AS * 4 <= kTile * 2, "two accumulator slices per K buffer");
+    const float m_row = pair_max32(m_lane[0]);
+    const float l_row = pair_sum32(l_run[0]);
+    if (hi == 0) {
+      st[wave * 32 + l32] = ref[0];
+      st[kWaves * 32 + wave * 32 + l32] = m_row;
+      st[2 * kWaves * 32 + wave * 32 + l32] = l_row;
+    }
+    __syncthreads();
+    float M = -INFINITY, mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      M = fmaxf(M, st[w * 32 + l32]);
+      mm = fmaxf(mm, st[kWaves * 32 + w * 32 + l32]);
+    }
+    const float f = fast_exp2(ref[0] - M);  // 0 for a wave that saw no key
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 w4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w4[e] = acc[0][db][4 * r4 + e] * f;
+        *reinterpret_cast<f32x4*>(sacc + l32 * AS + db * 32 + 8 * r4 + 4 * hi) = w4;
+      }
+    __syncthreads();
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      L += st[2 * kWaves * 32 + w * 32 + l32] * fast_exp2(st[w * 32 + l32] - M);
+    const float inv = 1.f / L;
+    const int row = q0 + l32;
+    if (row < n_q) {
+      // this lane: row l32, columns col0 .. col0 + D/8 (wave's quarter, lane half hi)
+      constexpr int CPL = D / 8;
+      const int col0 = wave * (D / 4) + hi * CPL;
+      const int64_t grow = (int64_t)bh * n_q + row;
+      const int64_t prow = (int64_t)sp * a.rows + grow;
+#pragma unroll
+      for (int c = 0; c < CPL; c += 4) {
+        f32x4 sum = f32x4{};
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float* sl = reinterpret_cast<const float*>(w < 2 ? sK0 : sK1) + (w & 1) * 32 * AS;
+          sum += *reinterpret_cast<const f32x4*>(sl + l32 * AS + col0 + c);
+        }
+        if (a.Po == nullptr) {
+          bf16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (bf16)(sum[e] * inv);
+          *reinterpret_cast<bf16x4*>(a.O + grow * D + col0 + c) = o;
+        } else {
+          *reinterpret_cast<f32x4*>(a.Po + prow * D + col0 + c) = sum * inv;
+        }
+      }
+      if (wave == 0 && hi == 0) {
+        if (a.Po == nullptr) {
+          if (a.Mx != nullptr) {
+            a.Mx[grow] = mm * a.scale;
+            a.Ls[grow] = L * fast_exp2(-__builtin_fmaf(mm, C, -M));
+          }
+        } else {
+          *reinterpret_cast<f32x4*>(a.Ps + prow * 4) = f32x4{mm, M, L, 0.f};
+        }
+      }
+    }
+    return;
   }
 
   // epilogue: O = acc / l, written once; statistics for the exact maximum
@@ -325,9 +415,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(const FwdArgs a) 
   }
 }
 
-template <int D, int QB, int BC>
+template <int D, int QB, int BC, bool kDecode>
 hipError_t launch(const FwdProblem& p, hipStream_t stream) {
-  constexpr int kBQ = kWaves * QB * 32;
+  constexpr int kBQ = kDecode ? 32 : kWaves * QB * 32;
   FwdArgs a;
   a.Q = static_cast<const bf16*>(p.q);
   a.K = static_cast<const bf16*>(p.k);
@@ -347,22 +437,31 @@ hipError_t launch(const FwdProblem& p, hipStream_t stream) {
   a.total = (int)total;
   a.scale = 1.0f / sqrtf((float)D);
   a.C = kLog2e * a.scale;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BC>), dim3((unsigned)total), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BC, kDecode>), dim3((unsigned)total), dim3(kThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
-// d = 64: 256 query rows and 128-key tiles per workgroup; d = 128: 128 rows, 64 keys
+// d = 64: 256 query rows and 128-key tiles per workgroup; d = 128: 128 rows, 64 keys.
+// Heads with at most kDecodeRows query rows use the decoding mode (32 rows,
+// 128-key tiles, keys split across the waves).
 constexpr int kQB64 = 2, kBC64 = 128, kQB128 = 1, kBC128 = 64;
+constexpr int kDecodeRows = 64;
 
 }  // namespace
 
-FwdGeometry fwd_geometry_bf16(int d) {
+FwdGeometry fwd_geometry_bf16(int d, int64_t rows_q) {
+  if (rows_q <= kDecodeRows) return FwdGeometry{32, 32 * kWaves};
   return d == 64 ? FwdGeometry{kWaves * kQB64 * 32, kBC64} : FwdGeometry{kWaves * kQB128 * 32, kBC128};
 }
 
 hipError_t launch_fwd_bf16(int d, const FwdProblem& p, hipStream_t stream) {
-  if (d == 64) return launch<64, kQB64, kBC64>(p, stream);
-  return launch<128, kQB128, kBC128>(p, stream);
+  if (p.rows_q <= kDecodeRows) {
+    if (d == 64) return launch<64, 1, 32 * kWaves, true>(p, stream);
+    return launch<128, 1, 32 * kWaves, true>(p, stream);
+  }
+  if (d == 64) return launch<64, kQB64, kBC64, false>(p, stream);
+  return launch<128, kQB128, kBC128, false>(p, stream);
 }
 
 }  // namespace mea

@@ -40,9 +40,12 @@ struct FwdGeometry {
   int query_rows;  // query rows per workgroup
   int key_tile;    // keys per LDS tile (split lengths are multiples of it)
 };
-FwdGeometry fwd_geometry_bf16(int d);
+// (the bf16 forward picks a decoding layout for heads with few query rows)
+FwdGeometry fwd_geometry_bf16(int d, int64_t rows_q);
 FwdGeometry fwd_geometry_f32(int d);
-inline FwdGeometry fwd_geometry(bool bf16, int d) { return bf16 ? fwd_geometry_bf16(d) : fwd_geometry_f32(d); }
+inline FwdGeometry fwd_geometry(bool bf16, int d, int64_t rows_q) {
+  return bf16 ? fwd_geometry_bf16(d, rows_q) : fwd_geometry_f32(d);
+}
 
 // Forward pass (final or, with p.splits > 1, partial) for bf16 / fp32 inputs.
 hipError_t launch_fwd_bf16(int d, const FwdProblem& p, hipStream_t stream);

@@ -215,7 +215,9 @@ def split(L, dt=BF16, B=1, H=1, H_kv=1, n_q=1, n_k=16384, d=64, q=A, k=A, v=A, o
     return L.attn_fwd_splitkv(dt, B, H, H_kv, n_q, n_k, d, q, k, v, o, m, l, s, ws, wsb, None)
 
 
-@pytest.mark.parametrize("dt,d,tile", [(BF16, 64, 128), (BF16, 128, 64), (F32, 64, 32), (F32, 128, 32)])
+# key tile of the split ranges at one query row per head: bf16 then uses its decoding
+# layout (128-key tiles at both d); fp32 always 32
+@pytest.mark.parametrize("dt,d,tile", [(BF16, 64, 128), (BF16, 128, 128), (F32, 64, 32), (F32, 128, 32)])
 def test_split_planning(L, dt, d, tile):
     ns = mea.attn_fwd_splitkv_num_splits
     wsb = mea.attn_fwd_splitkv_workspace_bytes
@@ -235,6 +237,15 @@ def test_split_planning(L, dt, d, tile):
     assert ns(dt, 1, 1, 1, 1, 4096, d, -1) == 0
     assert wsb(dt, 1, 1, 1, 1, 4096, d, -1) == 0
     assert ns(dt, 1, 3, 2, 1, 4096, d, 0) == 0           # invalid grouping
+
+
+def test_split_planning_full_tiles(L):
+    # more than 64 query rows per head: the regular layouts (bf16 d = 128 uses 64-key tiles)
+    ns = mea.attn_fwd_splitkv_num_splits
+    assert ns(BF16, 1, 1, 1, 4096, 4096, 128, 10 ** 6) == 4096 // 64
+    assert ns(BF16, 1, 1, 1, 4096, 4096, 64, 10 ** 6) == 4096 // 128
+    assert ns(BF16, 1, 1, 1, 65, 4096, 128, 10 ** 6) == 4096 // 64
+    assert ns(BF16, 1, 1, 1, 64, 4096, 128, 10 ** 6) == 4096 // 128   # still decoding
 
 
 def test_split_validation(L):
