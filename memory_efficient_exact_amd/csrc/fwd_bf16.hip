@@ -451,8 +451,8 @@ constexpr int kDecodeRows = 64;
 }  // namespace
 
 FwdGeometry fwd_geometry_bf16(int d, int64_t rows_q) {
-  if (rows_q <= kDecodeRows) return FwdGeometry{32, 32 * kWaves};
-  return d == 64 ? FwdGeometry{kWaves * kQB64 * 32, kBC64} : FwdGeometry{kWaves * kQB128 * 32, kBC128};
+  if (rows_q <= kDecodeRows) return FwdGeometry{32, 32 * kWaves, d == 64 ? 2 : 1};
+  return d == 64 ? FwdGeometry{kWaves * kQB64 * 32, kBC64, 2} : FwdGeometry{kWaves * kQB128 * 32, kBC128, 2};
 }
 
 hipError_t launch_fwd_bf16(int d, const FwdProblem& p, hipStream_t stream) {

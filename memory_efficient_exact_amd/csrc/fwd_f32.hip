@@ -256,7 +256,7 @@ hipError_t launch(const FwdProblem& p, hipStream_t stream) {
 
 }  // namespace
 
-FwdGeometry fwd_geometry_f32(int) { return FwdGeometry{kBQ, kBC}; }
+FwdGeometry fwd_geometry_f32(int) { return FwdGeometry{kBQ, kBC, 2}; }
 
 hipError_t launch_fwd_f32(int d, const FwdProblem& p, hipStream_t stream) {
   if (d == 64) return launch<64>(p, stream);

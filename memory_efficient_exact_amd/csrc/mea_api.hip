@@ -18,11 +18,11 @@ constexpr int64_t kMaxN = int64_t(1) << 24;
 constexpr int64_t kMaxBH = int64_t(1) << 24;
 constexpr int64_t kMaxBlocks = int64_t(1) << 23;
 // Split-key planning: at most this many key ranges per head; the automatic
-// choice splits only grids of fewer than this many workgroups (two per
-// compute unit, what the forward kernels keep resident) and keeps at least
-// two key tiles in every range.
+// choice splits only grids smaller than one full round of resident
+// workgroups (compute units x the forward kernel's workgroups per CU) and
+// keeps at least two key tiles in every range.
 constexpr int64_t kMaxSplits = 256;
-constexpr int64_t kAutoWorkgroups = 512;
+constexpr int64_t kComputeUnits = 256;
 constexpr int64_t kAutoMinTiles = 2;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -100,7 +100,7 @@ SplitPlan plan_splits(const Shape& s, int64_t requested) {
   int64_t want = requested;
   if (want <= 0) {
     const int64_t base = s.heads * cdiv(s.rows_q, g.query_rows);
-    want = std::min(cdiv(kAutoWorkgroups, base), std::max<int64_t>(1, tiles_k / kAutoMinTiles));
+    want = std::min(cdiv(kComputeUnits * g.resident, base), std::max<int64_t>(1, tiles_k / kAutoMinTiles));
   }
   want = std::max<int64_t>(1, std::min({want, tiles_k, kMaxSplits}));
   p.split_len = cdiv(tiles_k, want) * g.key_tile;  // whole key tiles per range

@@ -39,6 +39,7 @@ struct FwdProblem {
 struct FwdGeometry {
   int query_rows;  // query rows per workgroup
   int key_tile;    // keys per LDS tile (split lengths are multiples of it)
+  int resident;    // workgroups that fit on one compute unit at once
 };
 // (the bf16 forward picks a decoding layout for heads with few query rows)
 FwdGeometry fwd_geometry_bf16(int d, int64_t rows_q);
