@@ -1,6 +1,7 @@
 // Device-side building blocks for the gfx950 attention kernels: vector types,
-// MFMA wrappers with their lane layouts, the LDS tile swizzle, transposed LDS
-// reads and wave-level helpers. Host code never includes this file.
+// MFMA wrappers with their lane layouts, the padded LDS tile layout,
+// transposed LDS reads, direct global-to-LDS copies and wave-level helpers.
+// Host code never includes this file.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,7 +17,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define MEA_LDS __attribute__((address_space(3)))
 
@@ -47,23 +47,6 @@ __device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
 }
 
 // ---------------------------------------------------------------- LDS tiles
-// A bf16 tile of R rows x D columns is stored row-major in LDS, one row after
-// another, with its 16-byte chunks permuted inside each row by XOR with a
-// row-dependent key. The permutation keeps 8-byte halves together, so both
-// 16-byte row reads and 8-byte transposed reads see whole pieces. Keys spread
-// 16 consecutive rows at the same logical chunk over all 64 banks.
-template <int D>
-__device__ __forceinline__ int swz_chunk(int row, int chunk) {
-  static_assert(D == 64 || D == 128, "head dimension");
-  return D == 64 ? (chunk ^ ((row >> 1) & 7)) : (chunk ^ (row & 15));
-}
-
-// element offset of (row, col) in a swizzled bf16 tile; col must be a multiple of 4
-template <int D>
-__device__ __forceinline__ int swz_off(int row, int col) {
-  return row * D + swz_chunk<D>(row, col >> 3) * 8 + (col & 7);
-}
-
 // Padded row-major bf16 tile: each row of D elements is followed by 16 bytes
 // of padding, so row r starts at byte r*(2D + 16). For D = 64 (144-byte rows)
 // consecutive rows start 36 banks apart: 16 rows read at the same 16-byte
