@@ -209,7 +209,8 @@ def naive_bwd(q, k, v, do, rows=None, cols=None, row_block=1024):
     complete within its block); dK and dV are sums over query rows and so are
     accumulated block by block. ``rows`` restricts dQ to those query rows and
     ``cols`` restricts dK, dV to those key rows (the full softmax is still
-    formed for every query row). Returns (dq, dk, dv).
+    formed for every query row that contributes; with an empty ``cols`` only
+    the blocks holding requested rows are visited). Returns (dq, dk, dv).
     """
     q3, lead = _as_slices(q)
     k3, _ = _as_slices(k)
@@ -229,9 +230,13 @@ def naive_bwd(q, k, v, do, rows=None, cols=None, row_block=1024):
     # position of each requested query row in the dq output
     want_row = np.full(n, -1, dtype=np.int64)
     want_row[ridx] = np.arange(ridx.shape[0])
+    # with no key rows requested, blocks holding no requested query row add nothing
+    only_rows = cidx.shape[0] == 0
     for g in range(G):
         for b0 in range(0, n, row_block):
             b1 = min(n, b0 + row_block)
+            if only_rows and not (want_row[b0:b1] >= 0).any():
+                continue
             s = (q3[g, b0:b1] @ k3[g].T) * scale
             p = np.exp(s - s.max(axis=1, keepdims=True))
             p /= p.sum(axis=1, keepdims=True)

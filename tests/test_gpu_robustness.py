@@ -1,0 +1,133 @@
+"""GPU checks beyond small-shape parity: the longest sequences (sampled rows
+against the fp64 oracle, and identities that hold at any length), concurrent
+calls on several streams, and calls captured in a HIP graph and replayed.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import inputgen
+import memory_efficient_exact_amd as mea
+import oracle
+
+from test_gpu_parity import check, check_stats, f64, gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype,n", [("bf16", 1 << 20), ("fp32", 1 << 18)])
+def test_forward_longest_sequence_sampled_rows(dtype, n):
+    # one head of 2^20 keys (bf16; 2^18 for the fp64-score fp32 path): row indices,
+    # tile offsets and grids far beyond every workload
+    say("fwd long", dtype, n)
+    t = inputgen.draw(1, 1, n, 64, dtype, seed=101)
+    o, m, l = mea.attn_fwd(gpu(t["q"]), gpu(t["k"]), gpu(t["v"]))
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.random.default_rng(102).choice(n, 14, replace=False), [0, n - 1]])
+    o_ref, m_ref, l_ref = oracle.naive_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), rows=rows)
+    check("O", f64(o.cpu())[:, :, rows], o_ref, dtype)
+    check_stats(m.cpu().numpy()[:, :, rows], l.cpu().numpy()[:, :, rows], m_ref, l_ref, dtype)
+
+
+def test_backward_long_sequence_rows_and_identities():
+    # 2^19 tokens: sampled dQ rows against the oracle; dK and dV through identities of
+    # the softmax Jacobian that hold at any length: sum_j dK_j = 0 (each softmax row is
+    # shift-invariant) and sum_j dV_j = sum_i dO_i (each row of P sums to 1)
+    n = 1 << 19
+    say("bwd long", n)
+    t = inputgen.draw(1, 1, n, 64, "bf16", seed=103, with_do=True)
+    q, k, v, do = (gpu(t[x]) for x in ("q", "k", "v", "do"))
+    o, m, l = mea.attn_fwd(q, k, v)
+    dq, dk, dv = mea.attn_bwd(q, k, v, o, do, m, l)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.random.default_rng(104).choice(n, 14, replace=False), [0, n - 1]])
+    rq, _, _ = oracle.naive_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]), rows=rows,
+                                cols=np.array([], dtype=np.int64), row_block=16)
+    check("dQ", f64(dq.cpu())[:, :, rows], rq, "bf16")
+    dk64, dv64, do64 = f64(dk.cpu())[0, 0], f64(dv.cpu())[0, 0], f64(t["do"])[0, 0]
+    assert np.all(np.isfinite(dk64)) and np.all(np.isfinite(dv64))
+    scale_k = np.abs(dk64).sum(axis=0)
+    scale_v = np.abs(dv64).sum(axis=0)
+    assert np.all(np.abs(dk64.sum(axis=0)) <= 1e-4 * scale_k), np.abs(dk64.sum(axis=0)).max()
+    assert np.all(np.abs(dv64.sum(axis=0) - do64.sum(axis=0)) <= 1e-4 * scale_v)
+
+
+def _step(t, outs=None, stream=None):
+    """Forward then backward on the given stream, into preallocated outputs."""
+    q, k, v, do = t
+    if outs is None:
+        outs = dict(o=torch.empty_like(q), m=torch.empty(q.shape[:3], device=q.device),
+                    l=torch.empty(q.shape[:3], device=q.device), dq=torch.empty_like(q),
+                    dk=torch.empty_like(k), dv=torch.empty_like(v),
+                    ws=torch.empty(mea.attn_bwd_workspace_bytes(mea.DTYPE_BF16, *q.shape),
+                                   dtype=torch.uint8, device=q.device))
+    mea.attn_fwd(q, k, v, out=outs["o"], row_max=outs["m"], row_sum=outs["l"], stream=stream)
+    mea.attn_bwd(q, k, v, outs["o"], do, outs["m"], outs["l"], dq=outs["dq"], dk=outs["dk"],
+                 dv=outs["dv"], workspace=outs["ws"], stream=stream)
+    return outs
+
+
+def test_concurrent_streams_match_sequential_bitwise():
+    # the library keeps no state: independent calls on two streams at once give the
+    # same bits as one after the other
+    say("two streams")
+    inputs = []
+    for seed in (111, 112):
+        t = inputgen.draw(2, 8, 2048, 64, "bf16", seed=seed, with_do=True)
+        inputs.append(tuple(gpu(t[x]) for x in ("q", "k", "v", "do")))
+    ref = [_step(t) for t in inputs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [None, None]
+    torch.cuda.synchronize()
+    for i in range(2):
+        with torch.cuda.stream(streams[i]):
+            outs[i] = _step(inputs[i], stream=streams[i])
+    torch.cuda.synchronize()
+    for r, o in zip(ref, outs):
+        for key in ("o", "m", "l", "dq", "dk", "dv"):
+            assert torch.equal(r[key], o[key]), key
+
+
+def test_graph_capture_replays_match_eager():
+    # forward, backward and the split-key forward captured in one HIP graph: every
+    # replay, with new inputs copied into the captured buffers and eager work and
+    # synchronisations in between, must give the eager result bit for bit
+    say("graph capture")
+    shape = (1, 4, 1000, 64)
+    bufs = [torch.empty(shape, dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    outs = _step(tuple(bufs))  # allocates every output outside the capture
+    sq = torch.empty_like(bufs[0])
+    sws = torch.empty(max(16, mea.attn_fwd_splitkv_workspace_bytes(mea.DTYPE_BF16, 1, 4, 4, 1000,
+                                                                   1000, 64, 4)),
+                      dtype=torch.uint8, device="cuda")
+    sm = torch.empty(shape[:3], device="cuda")
+    sl = torch.empty_like(sm)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            _step(tuple(bufs), outs)
+            mea.attn_fwd_splitkv(bufs[0], bufs[1], bufs[2], num_splits=4, out=sq, row_max=sm,
+                                 row_sum=sl, workspace=sws)
+    torch.cuda.synchronize()
+    for replay, seed in enumerate((121, 122, 123)):
+        t = inputgen.draw(*shape, "bf16", seed=seed, with_do=True)
+        for b, name in zip(bufs, ("q", "k", "v", "do")):
+            b.copy_(t[name])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eager = _step(tuple(x.clone() for x in bufs))
+        eo, em, el = mea.attn_fwd_splitkv(bufs[0], bufs[1], bufs[2], num_splits=4)
+        torch.cuda.synchronize()
+        for key in ("o", "m", "l", "dq", "dk", "dv"):
+            assert torch.equal(outs[key], eager[key]), (replay, key)
+        assert torch.equal(sq, eo) and torch.equal(sm, em) and torch.equal(sl, el), replay
+        o_ref, _, _ = oracle.naive_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]))
+        check("O replay", f64(outs["o"].cpu()), o_ref, "bf16")

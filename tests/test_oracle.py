@@ -365,3 +365,15 @@ def test_fp32_scores_cannot_meet_1e5_on_stress_inputs_but_fp64_scores_can():
     err64 = np.abs(o - ref).max()
     assert err32 > 1e-5, err32
     assert err64 < 2e-6, err64
+
+
+def test_backward_rows_only_equals_full():
+    # an empty cols list visits only the blocks holding the requested rows
+    rng = np.random.default_rng(204)
+    q, k, v, do = (rng.standard_normal((2, 50, 8)) for _ in range(4))
+    dq, _, _ = oracle.naive_bwd(q, k, v, do)
+    rows = np.array([49, 3, 20])
+    dq2, dk2, dv2 = oracle.naive_bwd(q, k, v, do, rows=rows, cols=np.array([], dtype=np.int64),
+                                     row_block=7)
+    np.testing.assert_allclose(dq2, dq[:, rows], rtol=0, atol=1e-13)
+    assert dk2.shape == (2, 0, 8) and dv2.shape == (2, 0, 8)
