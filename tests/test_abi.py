@@ -273,3 +273,37 @@ def test_binding_rejects_bad_group_shapes():
         mea.attn_fwd_ex(q, k, k)  # CPU tensors
     with pytest.raises(ValueError):
         mea.attn_fwd_splitkv(q, k, k[..., :32])
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include "mea.h"
+int main(void) {
+  char buf[16] __attribute__((aligned(16)));
+  void* p = buf;
+  /* validation paths only: no call below reaches a kernel launch */
+  if (mea_version() != 200) return 1;
+  if (attn_fwd(MEA_DTYPE_BF16, 1, 1, 8, 96, p, p, p, p, NULL, NULL, NULL) != MEA_ERR_UNSUPPORTED) return 2;
+  if (attn_fwd_ex(MEA_DTYPE_F32, 1, 4, 3, 8, 8, 64, p, p, p, p, NULL, NULL, NULL) != MEA_ERR_SHAPE) return 3;
+  if (attn_bwd(MEA_DTYPE_BF16, 0, 1, 8, 64, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
+               NULL, NULL, 0, NULL) != MEA_OK) return 4;
+  if (attn_bwd_workspace_bytes(MEA_DTYPE_F32, 2, 8, 100, 128) != (size_t)16 * 2 * 8 * 100) return 5;
+  if (attn_fwd_splitkv_num_splits(MEA_DTYPE_BF16, 1, 32, 8, 1, 16384, 128, 0) < 2) return 6;
+  printf("%s\n", attn_status_str(MEA_ERR_WORKSPACE));
+  return 0;
+}
+"""
+
+
+def test_header_compiles_as_c99_and_links(tmp_path):
+    src = tmp_path / "abi.c"
+    exe = tmp_path / "abi"
+    src.write_text(C_PROGRAM)
+    libdir = os.path.dirname(mea.library_path())
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        str(src), "-o", str(exe), "-L", libdir, "-lmea", f"-Wl,-rpath,{libdir}"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, (r.returncode, r.stderr)
+    assert r.stdout.strip() == "MEA_ERR_WORKSPACE"
