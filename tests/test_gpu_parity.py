@@ -300,3 +300,40 @@ def test_forward_allocates_nothing_beyond_outputs():
     assert torch.cuda.max_memory_allocated() == before
     # the only state beyond Q, K, V, O is 8 bytes per row of statistics
     assert m.numel() * 4 + l.numel() * 4 == 8 * w.B * w.H * w.n
+
+
+def test_bench_step_workload_backward():
+    # the step bench.py times: 1 x 16 x 16384 x 64 bf16, inputs drawn exactly as the bench
+    # draws them, forward with statistics then backward with a caller workspace
+    w = inputgen.WORKLOADS["c3_long_bf16"]
+    say("bench step fwd+bwd", w.name)
+    t = inputgen.draw(w.B, w.H, w.n, w.d, w.dtype, seed=w.seed, with_do=True)
+    q, k, v, do = (gpu(t[x]) for x in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    m = torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)
+    l = torch.empty_like(m)
+    ws = torch.empty(mea.attn_bwd_workspace_bytes(mea.DTYPE_BF16, w.B, w.H, w.n, w.d),
+                     dtype=torch.uint8, device=DEV)
+    mea.attn_fwd(q, k, v, out=o, row_max=m, row_sum=l)
+    dq, dk, dv = mea.attn_bwd(q, k, v, o, do, m, l, workspace=ws)
+    torch.cuda.synchronize()
+    dq, dk, dv = (f64(x.cpu()) for x in (dq, dk, dv))
+    rows = sample_rows(w.n, 24, w.seed + 2)
+    cols = sample_rows(w.n, 24, w.seed + 3)
+    q64, k64, v64, do64 = (f64(t[x]) for x in ("q", "k", "v", "do"))
+    # dQ rows on every head (each row needs only its own softmax)
+    rq, _, _ = oracle.naive_bwd(q64, k64, v64, do64, rows=rows, cols=np.array([], dtype=np.int64),
+                                row_block=64)
+    check("dQ", dq[:, :, rows], rq, "bf16")
+    # dK, dV key rows on two heads (every query row contributes)
+    for h in (0, 11):
+        sl = (slice(0, 1), slice(h, h + 1))
+        _, rk, rv = oracle.naive_bwd(q64[sl], k64[sl], v64[sl], do64[sl], rows=rows[:1], cols=cols)
+        check("dK", dk[sl][:, :, cols], rk, "bf16")
+        check("dV", dv[sl][:, :, cols], rv, "bf16")
+    # identities on every head: sum_j dK_j = 0, sum_j dV_j = sum_i dO_i
+    for h in range(w.H):
+        sk = np.abs(dk[0, h]).sum(axis=0)
+        sv = np.abs(dv[0, h]).sum(axis=0)
+        assert np.all(np.abs(dk[0, h].sum(axis=0)) <= 1e-3 * sk), h
+        assert np.all(np.abs(dv[0, h].sum(axis=0) - do64[0, h].sum(axis=0)) <= 1e-3 * sv), h
