@@ -15,6 +15,11 @@
 // distinct banks. The score tile is transposed (lane = query), so the per-row
 // state lives in registers; four lanes (l, l^16, l^32, l^48) share a query.
 //
+// Decoding mode (at most 32 query rows per head): the four waves share one
+// 16-row query block and each takes a different 16-key block of every 64-key
+// tile, so no fp64 MFMA work goes to padding query rows; their partial
+// results merge through LDS after the sweep.
+//
 // Key ranges (split-key mode): a workgroup may cover only keys
 // [key0, key0 + split_len) of its head and then writes that range's summary, the
 // fp32 row acc / l, the fp64 maximum m and l (relative to m), for the merge
@@ -29,6 +34,9 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBQ = 16 * kWaves;  // query rows per workgroup
 constexpr int kBC = 32;           // keys per tile
+constexpr int kBQDecode = 16;     // decoding: query rows per workgroup
+constexpr int kBCDecode = 64;     // decoding: keys per tile (one 16-key block per wave)
+constexpr int kDecodeRows = 32;   // heads with at most this many query rows decode
 
 __device__ __forceinline__ float xor16f(float x) { return __shfl_xor(x, 16, 64); }
 __device__ __forceinline__ double xor16d(double x) { return __shfl_xor(x, 16, 64); }
@@ -54,19 +62,21 @@ struct FwdArgs32 {
   double scale64;  // 1 / sqrt(D)
 };
 
-template <int D>
+template <int D, bool kDecode>
 __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs32 a) {
   constexpr int KS = D + 4;   // K row stride (floats): 16-byte pad
   constexpr int VS = D + 16;  // V row stride (floats): 64-byte pad
   constexpr int KK = D / 4;   // k-steps of the fp64 score MFMA
   constexpr int DB = D / 16;  // 16-wide output column blocks
-  constexpr int KB = kBC / 16;
+  constexpr int BC = kDecode ? kBCDecode : kBC;  // keys per tile
+  constexpr int BQ = kDecode ? kBQDecode : kBQ;  // query rows per workgroup
+  constexpr int KB = kDecode ? 1 : BC / 16;      // 16-key blocks per wave per tile
   constexpr int kCPR = D / 4;  // 16-byte chunks per row
-  constexpr int kLoads = kBC * D / 4 / kThreads;
-  static_assert(kLoads * 4 * kThreads == kBC * D, "tile split");
+  constexpr int kLoads = BC * D / 4 / kThreads;
+  static_assert(kLoads * 4 * kThreads == BC * D, "tile split");
 
-  __shared__ __attribute__((aligned(16))) float sK[2][kBC * KS];
-  __shared__ __attribute__((aligned(16))) float sV[2][kBC * VS];
+  __shared__ __attribute__((aligned(16))) float sK[2][BC * KS];
+  __shared__ __attribute__((aligned(16))) float sV[2][BC * VS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -86,7 +96,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs32 a) {
   const double C64 = a.C64;
   const float* Kh = a.K + ((int64_t)bh * a.n_k + key0) * D;
   const float* Vh = a.V + ((int64_t)bh * a.n_k + key0) * D;
-  const int row = qt * kBQ + wave * 16 + l16;  // this lane's query row
+  const int row = kDecode ? qt * BQ + l16 : qt * BQ + wave * 16 + l16;  // this lane's query row
+  const int blk0 = kDecode ? wave : 0;  // first 16-key block of a tile this wave takes
   const int64_t grow = (int64_t)bh * n_q + row;
 
   // B operand of S^T = K Q^T: Q[row][4*kk + g4] as fp64
@@ -129,35 +140,35 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs32 a) {
     }
   };
 
-  const int ntiles = (n + kBC - 1) / kBC;
+  const int ntiles = (n + BC - 1) / BC;
   gload(0);
   swrite(0);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    const int j0 = t * kBC;
-    if (t + 1 < ntiles) gload(j0 + kBC);
+    const int j0 = t * BC;
+    if (t + 1 < ntiles) gload(j0 + BC);
     const float* ks = sK[buf];
     const float* vs = sV[buf];
 
-    // S^T block kb: lane holds query l16 and, in register r, key 16*kb + 4*r + g4
+    // S^T block kb: lane holds query l16 and, in register r, key 16*(blk0+kb) + 4*r + g4
     f64x4 s[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       s[kb] = f64x4{};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const double a = (double)ks[(kb * 16 + l16) * KS + 4 * kk + g4];
+        const double a = (double)ks[((blk0 + kb) * 16 + l16) * KS + 4 * kk + g4];
         s[kb] = mfma_f64_16x16x4(a, qd[kk], s[kb]);
       }
     }
-    if (j0 + kBC > n) {
+    if (j0 + BC > n) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (j0 + kb * 16 + 4 * r + g4 >= n) s[kb][r] = -INFINITY;
+          if (j0 + (blk0 + kb) * 16 + 4 * r + g4 >= n) s[kb][r] = -INFINITY;
     }
 
     double mx = s[0][0];
@@ -168,14 +179,17 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs32 a) {
     mx = fmax(mx, xor16d(mx));
     mx = fmax(mx, xor32d(mx));
     const double m_new = fmax(m_run, mx);
-    const float alpha = fast_exp2((float)((m_run - m_new) * C64));
+    // a wave that has seen no valid key yet (possible when decoding, where each
+    // wave covers one block of the tile) keeps weights and rescale at exactly 0
+    const double m_base = m_new == -INFINITY ? 0.0 : m_new;
+    const float alpha = fast_exp2((float)((m_run - m_base) * C64));
     float p[KB][4];
     float ls = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[kb][r] = fast_exp2((float)((s[kb][r] - m_new) * C64));
+        p[kb][r] = fast_exp2((float)((s[kb][r] - m_base) * C64));
         ls += p[kb][r];
       }
     l_run = l_run * alpha + ls;
@@ -189,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs32 a) {
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const float* vrow = vs + (kb * 16 + 4 * c + g4) * VS + l16;
+        const float* vrow = vs + ((blk0 + kb) * 16 + 4 * c + g4) * VS + l16;
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[db] = mfma_f32_16x16x4(vrow[db * 16], p[kb][c], acc[db]);
       }
@@ -201,6 +215,73 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs32 a) {
   // lanes l, l^16, l^32, l^48 share query l16: combine their partial sums
   float l_tot = l_run + xor16f(l_run);
   l_tot = l_tot + xor32(l_tot);
+
+  if constexpr (kDecode) {
+    // Merge the four waves (same 16 query rows, different keys). The loop ended
+    // with a barrier, so the tile buffers are free: per-wave maxima and sums go
+    // to sK[0], each wave's re-based accumulator (16 rows x D) to sV[0].
+    constexpr int AS = D + 4;
+    static_assert(kWaves * 16 * AS <= BC * VS, "accumulators fit one V buffer");
+    double* sm = reinterpret_cast<double*>(sK[0]);
+    float* sl = sK[0] + 2 * kWaves * 16;
+    float* sacc = sV[0];
+    if (g4 == 0) {
+      sm[wave * 16 + l16] = m_run;
+      sl[wave * 16 + l16] = l_tot;
+    }
+    __syncthreads();
+    double M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmax(M, sm[w * 16 + l16]);
+    const float f = m_run == -INFINITY ? 0.f : fast_exp2((float)((m_run - M) * C64));
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      *reinterpret_cast<f32x4*>(sacc + (wave * 16 + l16) * AS + db * 16 + 4 * g4) = acc[db] * f;
+    __syncthreads();
+    // this lane: query row lane / 4 of the block, D/16 columns of the wave's quarter
+    constexpr int CPL = D / 16;
+    const int qr = lane >> 2;
+    const int col0 = wave * (D / 4) + (lane & 3) * CPL;
+    const int qrow = qt * BQ + qr;
+    float L = 0.f;
+    double Mq = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) Mq = fmax(Mq, sm[w * 16 + qr]);
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const double mw = sm[w * 16 + qr];
+      L += mw == -INFINITY ? 0.f : sl[w * 16 + qr] * fast_exp2((float)((mw - Mq) * C64));
+    }
+    if (qrow < n_q) {
+      const int64_t gq = (int64_t)bh * n_q + qrow;
+      const int64_t oq = a.Po == nullptr ? gq : (int64_t)sp * a.rows + gq;
+      float* orow = (a.Po == nullptr ? a.O : a.Po) + oq * D;
+      const float inv = 1.f / L;
+#pragma unroll
+      for (int c = 0; c < CPL; c += 4) {
+        f32x4 sum = f32x4{};
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+          sum += *reinterpret_cast<const f32x4*>(sacc + (w * 16 + qr) * AS + col0 + c);
+        *reinterpret_cast<f32x4*>(orow + col0 + c) = sum * inv;
+      }
+      if (wave == 0 && (lane & 3) == 0) {
+        if (a.Po != nullptr) {
+          float* rec = a.Ps + oq * 4;
+          *reinterpret_cast<double*>(rec) = Mq;
+          rec[2] = L;
+          rec[3] = 0.f;
+        } else if (a.Mx != nullptr) {
+          const double m_nat = Mq * a.scale64;
+          const float m_st = (float)m_nat;
+          a.Mx[gq] = m_st;
+          a.Ls[gq] = (float)((double)L * exp(m_nat - (double)m_st));
+        }
+      }
+    }
+    return;
+  }
+
   const float inv = 1.f / l_tot;
   if (row < n_q) {
     // acc[db] register r holds O[row][16*db + 4*g4 + r]
@@ -229,8 +310,9 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs32 a) {
   }
 }
 
-template <int D>
+template <int D, bool kDecode>
 hipError_t launch(const FwdProblem& p, hipStream_t stream) {
+  constexpr int BQ = kDecode ? kBQDecode : kBQ;
   FwdArgs32 a;
   a.Q = static_cast<const float*>(p.q);
   a.K = static_cast<const float*>(p.k);
@@ -241,7 +323,7 @@ hipError_t launch(const FwdProblem& p, hipStream_t stream) {
   a.rows = p.heads * p.rows_q;
   a.n_q = p.rows_q;
   a.n_k = p.n_k;
-  a.qtiles = (p.rows_q + kBQ - 1) / kBQ;
+  a.qtiles = (p.rows_q + BQ - 1) / BQ;
   a.splits = p.splits > 1 ? p.splits : 1;
   a.split_len = p.splits > 1 ? p.split_len : p.n_k;
   a.Po = p.splits > 1 ? p.part : nullptr;
@@ -250,17 +332,21 @@ hipError_t launch(const FwdProblem& p, hipStream_t stream) {
   a.total = (int)total;
   a.scale64 = 1.0 / sqrt((double)D);
   a.C64 = 1.4426950408889634 * a.scale64;
-  hipLaunchKernelGGL((fwd_f32_kernel<D>), dim3((unsigned)total), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_f32_kernel<D, kDecode>), dim3((unsigned)total), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-FwdGeometry fwd_geometry_f32(int) { return FwdGeometry{kBQ, kBC, 2}; }
+FwdGeometry fwd_geometry_f32(int d, int64_t rows_q) {
+  // decoding at d = 128 double-buffers 64-key tiles in 141 KiB of LDS: one workgroup per CU
+  if (rows_q <= kDecodeRows) return FwdGeometry{kBQDecode, kBCDecode, d == 64 ? 2 : 1};
+  return FwdGeometry{kBQ, kBC, 2};
+}
 
 hipError_t launch_fwd_f32(int d, const FwdProblem& p, hipStream_t stream) {
-  if (d == 64) return launch<64>(p, stream);
-  return launch<128>(p, stream);
+  if (p.rows_q <= kDecodeRows) return d == 64 ? launch<64, true>(p, stream) : launch<128, true>(p, stream);
+  return d == 64 ? launch<64, false>(p, stream) : launch<128, false>(p, stream);
 }
 
 }  // namespace mea

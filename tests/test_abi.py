@@ -215,9 +215,9 @@ def split(L, dt=BF16, B=1, H=1, H_kv=1, n_q=1, n_k=16384, d=64, q=A, k=A, v=A, o
     return L.attn_fwd_splitkv(dt, B, H, H_kv, n_q, n_k, d, q, k, v, o, m, l, s, ws, wsb, None)
 
 
-# key tile of the split ranges at one query row per head: bf16 then uses its decoding
-# layout (128-key tiles at both d); fp32 always 32
-@pytest.mark.parametrize("dt,d,tile", [(BF16, 64, 128), (BF16, 128, 128), (F32, 64, 32), (F32, 128, 32)])
+# key tile of the split ranges at one query row per head: both forwards then use their
+# decoding layouts (bf16: 128-key tiles, fp32: 64-key tiles)
+@pytest.mark.parametrize("dt,d,tile", [(BF16, 64, 128), (BF16, 128, 128), (F32, 64, 64), (F32, 128, 64)])
 def test_split_planning(L, dt, d, tile):
     ns = mea.attn_fwd_splitkv_num_splits
     wsb = mea.attn_fwd_splitkv_workspace_bytes
@@ -246,6 +246,9 @@ def test_split_planning_full_tiles(L):
     assert ns(BF16, 1, 1, 1, 4096, 4096, 64, 10 ** 6) == 4096 // 128
     assert ns(BF16, 1, 1, 1, 65, 4096, 128, 10 ** 6) == 4096 // 64
     assert ns(BF16, 1, 1, 1, 64, 4096, 128, 10 ** 6) == 4096 // 128   # still decoding
+    assert ns(F32, 1, 1, 1, 4096, 4096, 128, 10 ** 6) == 4096 // 32
+    assert ns(F32, 1, 1, 1, 33, 4096, 64, 10 ** 6) == 4096 // 32
+    assert ns(F32, 1, 1, 1, 32, 4096, 64, 10 ** 6) == 4096 // 64     # fp32 decoding
 
 
 def test_split_validation(L):
