@@ -223,18 +223,58 @@ def sweep_split(steps, warmup):
     return {"mode": "splitkv", "steps": steps, "warmup": warmup, "rows": rows}
 
 
+def sweep_memory():
+    """Device memory of a forward and of a forward + backward at n = 1024 .. 16384
+    (B=1, H=16, d=64, bf16), outputs allocated by the binding: the peak beyond the
+    inputs and outputs (the method's overhead) must be the 8 bytes of row
+    statistics per query row, plus 8 more of backward workspace, at every n,
+    against 4*B*H*n^2 bytes for an fp32 score matrix."""
+    import torch
+
+    import inputgen
+    import memory_efficient_exact_amd as mea
+    dev = torch.device("cuda:0")
+    rows = []
+    for n in (1024, 2048, 4096, 8192, 16384):
+        B, H, d = 1, 16, 64
+        t = inputgen.draw(B, H, n, d, "bf16", seed=3000 + n, with_do=True)
+        q, k, v, do = (t[x].to(dev) for x in ("q", "k", "v", "do"))
+        io = q.numel() * q.element_size()
+        torch.cuda.synchronize(dev)
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
+        o, m, l = mea.attn_fwd(q, k, v)
+        torch.cuda.synchronize(dev)
+        fwd_over = torch.cuda.max_memory_allocated(dev) - base - io  # beyond the output O
+        dq, dk, dv = mea.attn_bwd(q, k, v, o, do, m, l)
+        torch.cuda.synchronize(dev)
+        step_over = torch.cuda.max_memory_allocated(dev) - base - 4 * io  # beyond O, dQ, dK, dV
+        row = {"n": n, "B": B, "H": H, "d": d, "fwd_overhead_bytes": fwd_over,
+               "fwd_overhead_per_row": fwd_over / (B * H * n),
+               "step_overhead_bytes": step_over,
+               "step_overhead_per_row": step_over / (B * H * n),
+               "n2_fp32_score_bytes": 4 * B * H * n * n}
+        rows.append(row)
+        log(json.dumps(row))
+        del t, q, k, v, do, o, m, l, dq, dk, dv
+        torch.cuda.empty_cache()
+    return {"mode": "memory", "rows": rows}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=("bench", "traffic", "configs", "splitkv"), default="bench",
+    ap.add_argument("--mode", choices=("bench", "traffic", "configs", "splitkv", "memory"), default="bench",
                     help="traffic: one 256 MiB copy (counter calibration) and one step, "
                          "for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs; configs: time "
                          "the forward on all five workloads (and the backward where the "
                          "workload trains), one JSON line with a row per workload; splitkv: "
-                         "unsplit vs split-key forward on small-grid and decoding shapes")
+                         "unsplit vs split-key forward on small-grid and decoding shapes; memory: "
+                         "device-memory overhead per query row at n = 1024 .. 16384")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the attention "
@@ -254,6 +294,9 @@ def main():
         return
     if args.mode == "splitkv":
         print(json.dumps(sweep_split(args.steps, args.warmup)), flush=True)
+        return
+    if args.mode == "memory":
+        print(json.dumps(sweep_memory()), flush=True)
         return
     w = inputgen.WORKLOADS["c3_long_bf16"]
     t = inputgen.draw(w.B, w.H, w.n, w.d, w.dtype, seed=w.seed, with_do=True)

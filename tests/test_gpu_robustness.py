@@ -1,9 +1,8 @@
 """GPU checks beyond small-shape parity: the longest sequences (sampled rows
 against the fp64 oracle, and identities that hold at any length), concurrent
-calls on several streams, and calls captured in a HIP graph and replayed.
+calls on several streams, calls captured in a HIP graph and replayed, and the
+device-memory overhead per query row at growing n.
 """
-
-import math
 
 import numpy as np
 import pytest
@@ -131,3 +130,24 @@ def test_graph_capture_replays_match_eager():
         assert torch.equal(sq, eo) and torch.equal(sm, em) and torch.equal(sl, el), replay
         o_ref, _, _ = oracle.naive_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]))
         check("O replay", f64(outs["o"].cpu()), o_ref, "bf16")
+
+
+@pytest.mark.parametrize("n", [1024, 4096, 16384])
+def test_memory_overhead_is_linear(n):
+    # beyond the inputs and the outputs, a forward keeps 8 bytes per query row (row max
+    # and row sum) and a backward adds 8 bytes per row of workspace: O(n), at every n
+    B, H, d = 1, 16, 64
+    say("memory", n)
+    t = inputgen.draw(B, H, n, d, "bf16", seed=131, with_do=True)
+    q, k, v, do = (gpu(t[x]) for x in ("q", "k", "v", "do"))
+    io = q.numel() * q.element_size()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    o, m, l = mea.attn_fwd(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.cuda.max_memory_allocated() - base - io == 8 * B * H * n
+    dq, dk, dv = mea.attn_bwd(q, k, v, o, do, m, l)
+    torch.cuda.synchronize()
+    assert torch.cuda.max_memory_allocated() - base - 4 * io == 16 * B * H * n
