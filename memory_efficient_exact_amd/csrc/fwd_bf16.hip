@@ -12,8 +12,8 @@
 // Layout of the work (per workgroup of 4 waves, two workgroups per CU):
 //  * each wave owns QB blocks of 32 query rows; the workgroup owns 4*QB*32;
 //  * K and V tiles of BC keys are copied straight from HBM into LDS
-//    (global_load_lds, no register staging), double-buffered, in a padded
-//    row-major layout (see Padded in mea_device.h);
+//    (global_load_lds, no register staging), double-buffered, in a swizzled
+//    row-major layout free of bank conflicts (see Swizzled in mea_device.h);
 //  * scores are formed transposed, S^T = K Q^T, on 32x32x16 bf16 MFMA, so
 //    that each lane holds one query's scores for 16 keys per 32-key block:
 //    the row maximum is a register reduction plus one v_permlane32_swap, and
@@ -85,7 +85,7 @@ struct FwdArgs {
 };
 
 // two workgroups per CU, except decoding at d = 128, whose 128-key tiles
-// (139 KiB of LDS double-buffered) leave room for one
+// (128 KiB of LDS double-buffered) leave room for one
 template <int D, int QB, int BC, bool kDecode>
 __global__ __launch_bounds__(kThreads, (kDecode && D == 128) ? 1 : 2) void fwd_bf16_kernel(const FwdArgs a) {
   static_assert(!kDecode || (QB == 1 && BC == 32 * kWaves), "decoding: one 32-key block per wave");
@@ -93,10 +93,9 @@ __global__ __launch_bounds__(kThreads, (kDecode && D == 128) ? 1 : 2) void fwd_b
   constexpr int DK = D / 16;             // k-steps of the score MFMA
   constexpr int DB = D / 32;             // 32-wide output column blocks
   constexpr int SB = BC / 32;            // 32-key blocks per LDS tile
-  using L = Padded<D>;
-  constexpr int RS = L::kRowElems;        // LDS row stride (elements)
-  constexpr int SPR = L::kSlotsPerRow;    // 16-byte slots per LDS row
-  constexpr int kTile = BC * RS;          // elements per K or V tile in LDS
+  using L = Swizzled<D>;
+  constexpr int SPR = L::kChunks;         // 16-byte chunks per LDS row
+  constexpr int kTile = BC * D;           // elements per K or V tile in LDS
   constexpr int NBLK = BC * SPR / 64;     // 1 KiB DMA blocks per tile
   constexpr int BPW = (NBLK + kWaves - 1) / kWaves;
   static_assert(NBLK * 64 == BC * SPR, "tile must be whole DMA blocks");
@@ -162,18 +161,18 @@ __global__ __launch_bounds__(kThreads, (kDecode && D == 128) ? 1 : 2) void fwd_b
   }
 
   // DMA of the K and V tile starting at key j0. Block b of a tile covers
-  // 16-byte LDS slots 64b..64b+63; slot s is row s / SPR, column chunk
-  // s % SPR of the padded layout. Pad slots fetch a duplicate of the row's
-  // first chunk (never read). Rows past n repeat row n-1 (their scores are
-  // masked to -inf, and their weights are exactly 0).
+  // 16-byte LDS slots 64b..64b+63; slot s holds row s / SPR at chunk
+  // position s % SPR, i.e. the row's chunk (s % SPR) ^ swz(row). Rows past n
+  // repeat row n-1 (their scores are masked to -inf, and their weights are
+  // exactly 0).
   int dma_row[BPW], dma_col[BPW];
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
     const int slot = (wave + kWaves * i) * 64 + lane;
     const int r = slot / SPR;
-    const int c = slot - r * SPR;
+    const int pc = slot - r * SPR;
     dma_row[i] = r;
-    dma_col[i] = (c == SPR - 1 ? 0 : c) * 8;
+    dma_col[i] = (pc ^ L::swz(r)) * 8;
   }
   auto issue = [&](bf16* kdst, bf16* vdst, int j0) {
 #pragma unroll
@@ -188,12 +187,20 @@ __global__ __launch_bounds__(kThreads, (kDecode && D == 128) ? 1 : 2) void fwd_b
     }
   };
 
-  // per-lane LDS offsets: K rows for the score MFMA, and the transposed-read
-  // pattern for V^T fragments (row 4*hi + jj/4, column 16*(g%2) + 4*(jj%4))
+  // per-lane LDS offsets: K rows for the score MFMA (row l32, columns
+  // 16*dk + 8*hi), and the transposed-read pattern for V^T fragments (rows
+  // 4*hi + jj/4 and 8 below it, columns 32*db + 16*(g%2) + 4*(jj%4)). Blocks
+  // of 16 rows further down add 16*D, which leaves the swizzle unchanged.
   const int g = lane >> 4;
   const int jj = lane & 15;
-  const int k_lane = L::off(l32, 8 * hi);
-  const int v_lane = L::off(4 * hi + (jj >> 2), (g & 1) * 16 + 4 * (jj & 3));
+  int k_off[DK], v_off[DB][2];
+#pragma unroll
+  for (int dk = 0; dk < DK; ++dk) k_off[dk] = L::off(l32, dk * 16 + 8 * hi);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      v_off[db][h] = L::off(4 * hi + (jj >> 2) + 8 * h, db * 32 + (g & 1) * 16 + 4 * (jj & 3));
 
   // One 32-key block: scores, online softmax, P V.
   auto block = [&](const bf16* ks, const bf16* vs, int sb, int j0, auto masked_tag) {
@@ -203,7 +210,7 @@ __global__ __launch_bounds__(kThreads, (kDecode && D == 128) ? 1 : 2) void fwd_b
     for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
 #pragma unroll
     for (int dk = 0; dk < DK; ++dk) {
-      const bf16x8 a = lds_read_b128(ks + k_lane + L::off(sb * 32, dk * 16));
+      const bf16x8 a = lds_read_b128(ks + sb * 32 * D + k_off[dk]);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) s[qb] = mfma32x32x16(a, qf[qb][dk], s[qb]);
     }
@@ -257,8 +264,8 @@ __global__ __launch_bounds__(kThreads, (kDecode && D == 128) ? 1 : 2) void fwd_b
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16* vp = vs + v_lane + L::off(sb * 32 + c * 16, db * 32);
-        const bf16x8 a = cat(lds_read_tr16(vp), lds_read_tr16(vp + 8 * RS));
+        const bf16* vp = vs + (sb * 32 + c * 16) * D;
+        const bf16x8 a = cat(lds_read_tr16(vp + v_off[db][0]), lds_read_tr16(vp + v_off[db][1]));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32x32x16(a, pf[qb][c], acc[qb][db]);
       }
@@ -296,12 +303,15 @@ __global__ __launch_bounds__(kThreads, (kDecode && D == 128) ? 1 : 2) void fwd_b
   if constexpr (kDecode) {
     // Merge the four waves' partial results (same 32 query rows, different
     // keys). The last step ended with a barrier and no DMA in flight, so the
-    // tile buffers are free: per-wave statistics go to sV0, each wave's
-    // re-based accumulator (32 rows x D fp32, rows padded) to sK0 / sK1.
+    // tile buffers are free: wave w's re-based accumulator (32 rows x D fp32,
+    // rows padded) goes to tile buffer w, the per-wave statistics to st.
     constexpr int AS = D + 4;
-    float* st = reinterpret_cast<float*>(sV0);  // [3][kWaves][32]: R, row max, row sum
-    float* sacc = reinterpret_cast<float*>(wave < 2 ? sK0 : sK1) + (wave & 1) * 32 * AS;
-    static_assert(2 * 32 * AS * 4 <= kTile * 2, "two accumulator slices per K buffer");
+    __shared__ float st[3 * kWaves * 32];  // [3][kWaves][32]: R, row max, row sum
+    auto slice = [&](int w) {
+      return reinterpret_cast<float*>(w == 0 ? sK0 : w == 1 ? sK1 : w == 2 ? sV0 : sV1);
+    };
+    float* sacc = slice(wave);
+    static_assert(32 * AS * 4 <= kTile * 2, "one accumulator slice per tile buffer");
     const float m_row = pair_max32(m_lane[0]);
     const float l_row = pair_sum32(l_run[0]);
     if (hi == 0) {
@@ -344,7 +354,7 @@ __global__ __launch_bounds__(kThreads, (kDecode && D == 128) ? 1 : 2) void fwd_b
         f32x4 sum = f32x4{};
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-          const float* sl = reinterpret_cast<const float*>(w < 2 ? sK0 : sK1) + (w & 1) * 32 * AS;
+          const float* sl = slice(w);
           sum += *reinterpret_cast<const f32x4*>(sl + l32 * AS + col0 + c);
         }
         if (a.Po == nullptr) {

@@ -1,5 +1,5 @@
 // Device-side building blocks for the gfx950 attention kernels: vector types,
-// MFMA wrappers with their lane layouts, the padded LDS tile layout,
+// MFMA wrappers with their lane layouts, the padded and swizzled LDS tile layouts,
 // transposed LDS reads, direct global-to-LDS copies and wave-level helpers.
 // Host code never includes this file.
 #pragma once
@@ -47,17 +47,47 @@ __device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
 }
 
 // ---------------------------------------------------------------- LDS tiles
-// Padded row-major bf16 tile: each row of D elements is followed by 16 bytes
-// of padding, so row r starts at byte r*(2D + 16). For D = 64 (144-byte rows)
-// consecutive rows start 36 banks apart: 16 rows read at the same 16-byte
-// column cover all 64 banks once, and the 4-row x 32-byte footprint of a
-// transposed read by 16 lanes is conflict-free as well. Every address is a
-// per-lane base plus compile-time offsets, with no swizzle arithmetic.
+// Padded row-major bf16 tile (used by the backward): each row of D elements is
+// followed by 16 bytes of padding, so row r starts at byte r*(2D + 16). For
+// D = 64 (144-byte rows) consecutive rows start 36 banks apart: 16 rows read
+// at the same 16-byte column cover all 64 banks once. A transposed read
+// serves 32 lanes (4 rows x 64 bytes) per pass, and there rows r and r + 2
+// overlap by 8 banks (a 2-way conflict; 4-way for D = 128). The backward was
+// measured no faster with the conflict-free layout below, so it keeps this
+// one, whose addresses are a per-lane base plus compile-time offsets.
 template <int D>
 struct Padded {
   static constexpr int kRowElems = D + 8;           // row stride in elements
   static constexpr int kSlotsPerRow = D / 8 + 1;    // 16-byte slots per row (last = pad)
   __device__ static constexpr int off(int row, int col) { return row * kRowElems + col; }
+};
+
+// Swizzled row-major bf16 tile (used by the forward): rows of D elements with no
+// padding; the 16-byte chunk c of row r sits at chunk position c ^ swz(r).
+// With 64 banks of 4 bytes, a 16-byte read of one chunk column by 16 lanes
+// (rows r..r+15) touches every bank once, and so does a transposed read by 32
+// lanes (4 rows x 64 bytes), which on the padded layout above overlaps
+// 2-way (D = 64) or 4-way (D = 128). swz permutes the chunks of a row, so
+// row offsets that are multiples of 16 keep it unchanged:
+//   D = 64  (two rows per 64 banks): swz(r) = bit-reverse of (r/2) mod 8
+//   D = 128 (one row per 64 banks):  swz(r) = bit-reverse of r mod 16
+template <int D>
+struct Swizzled {
+  static_assert(D == 64 || D == 128, "head dimension");
+  static constexpr int kChunks = D / 8;  // 16-byte chunks per row
+  __device__ static constexpr int swz(int r) {
+    if constexpr (D == 64) {
+      const int x = (r >> 1) & 7;
+      return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1);
+    } else {
+      const int x = r & 15;
+      return ((x & 1) << 3) | ((x & 2) << 1) | ((x & 4) >> 1) | ((x >> 3) & 1);
+    }
+  }
+  // element offset of (row, col); the 4 or 8 elements read from col on stay in one chunk
+  __device__ static constexpr int off(int row, int col) {
+    return row * D + (((col >> 3) ^ swz(row)) << 3) + (col & 7);
+  }
 };
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const bf16* p) {
