@@ -26,8 +26,12 @@
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
  *    the null stream). Nothing is synchronised. Inputs must stay valid and
  *    outputs untouched until the stream reaches the work.
+ *  - Outputs (o, row_max, row_sum, dq, dk, dv and the part of the workspace
+ *    a call uses) must not overlap one another or any input; inputs may share
+ *    memory (q == k == v is allowed). Overlaps are rejected with MEA_ERR_ALIAS.
  *  - Arguments are validated on the host before any HIP call, in this order:
- *    dtype, shape, head dimension, null pointers, alignment, workspace. A
+ *    dtype, shape, head dimension, null pointers, alignment, workspace,
+ *    overlap of outputs. A
  *    call with B, H or n equal to 0 does nothing and returns MEA_OK (pointers
  *    may then be NULL). MEA_ERR_LAUNCH reports a launch failure seen by
  *    hipGetLastError right after the launch; faults during execution surface
@@ -69,7 +73,8 @@ typedef enum {
   MEA_ERR_UNSUPPORTED = 3, /* unsupported dtype or head dimension d */
   MEA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   MEA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
-  MEA_ERR_LAUNCH = 6       /* the HIP runtime rejected a kernel launch */
+  MEA_ERR_LAUNCH = 6,      /* the HIP runtime rejected a kernel launch */
+  MEA_ERR_ALIAS = 7        /* an output overlaps an input or another output */
 } mea_status_t;
 
 /*

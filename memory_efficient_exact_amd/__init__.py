@@ -22,7 +22,7 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 
 _STATUS = ["MEA_OK", "MEA_ERR_NULL", "MEA_ERR_SHAPE", "MEA_ERR_UNSUPPORTED",
-           "MEA_ERR_ALIGN", "MEA_ERR_WORKSPACE", "MEA_ERR_LAUNCH"]
+           "MEA_ERR_ALIGN", "MEA_ERR_WORKSPACE", "MEA_ERR_LAUNCH", "MEA_ERR_ALIAS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None

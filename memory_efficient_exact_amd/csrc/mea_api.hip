@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0
+constexpr int kVersion = 300;  // 0.3.0
 // The largest grids are (heads * ceil(rows/64)) workgroups of 256 threads;
 // keep them (and all row indices) comfortably inside 32 bits.
 constexpr int64_t kMaxN = int64_t(1) << 24;
@@ -66,6 +66,39 @@ mea_status_t check_shape(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int
 // Backward workspace per query row: bf16 keeps {-D, lse2} as two floats; fp32
 // keeps lse2 in fp64 (scores of ~1e4 need more than fp32 there) and -D.
 size_t bwd_row_bytes(bool bf16) { return bf16 ? 8 : 16; }
+
+// Byte range [lo, hi) of one buffer of a call; empty ranges overlap nothing.
+struct Span {
+  uintptr_t lo = 0;
+  uintptr_t hi = 0;
+};
+Span span(const void* p, int64_t bytes) {
+  Span r;
+  if (p != nullptr && bytes > 0) {
+    r.lo = reinterpret_cast<uintptr_t>(p);
+    r.hi = r.lo + (uintptr_t)bytes;
+  }
+  return r;
+}
+bool overlap(const Span& a, const Span& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Every output must be disjoint from the other outputs and from every input
+// (the kernels read inputs while writing outputs); inputs may share memory.
+mea_status_t check_alias(std::initializer_list<Span> outputs, std::initializer_list<Span> inputs) {
+  for (auto o = outputs.begin(); o != outputs.end(); ++o) {
+    for (auto p = o + 1; p != outputs.end(); ++p)
+      if (overlap(*o, *p)) return MEA_ERR_ALIAS;
+    for (const Span& i : inputs)
+      if (overlap(*o, i)) return MEA_ERR_ALIAS;
+  }
+  return MEA_OK;
+}
+
+// Bytes of the query-side tensors (q, o, dO, dq), the key-side tensors (k, v,
+// dk, dv) and one per-row statistics array of a validated shape.
+int64_t q_bytes(const Shape& s) { return s.q_rows_total * s.d * (s.bf16 ? 2 : 4); }
+int64_t kv_bytes(const Shape& s) { return s.heads * s.n_k * s.d * (s.bf16 ? 2 : 4); }
+int64_t stat_bytes(const Shape& s) { return s.q_rows_total * 4; }
 
 mea_status_t check_ptrs(std::initializer_list<const void*> ptrs) {
   for (const void* p : ptrs)
@@ -143,6 +176,9 @@ mea_status_t fwd_impl(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_
   st = check_ptrs({q, k, v, o});
   if (st != MEA_OK) return st;
   if (row_max != nullptr && (!aligned16(row_max) || !aligned16(row_sum))) return MEA_ERR_ALIGN;
+  st = check_alias({span(o, q_bytes(s)), span(row_max, stat_bytes(s)), span(row_sum, stat_bytes(s))},
+                   {span(q, q_bytes(s)), span(k, kv_bytes(s)), span(v, kv_bytes(s))});
+  if (st != MEA_OK) return st;
   hipError_t e = run_fwd(s, fwd_problem(s, q, k, v, o, row_max, row_sum),
                          reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MEA_OK : MEA_ERR_LAUNCH;
@@ -165,6 +201,13 @@ mea_status_t bwd_impl(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return MEA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MEA_ERR_ALIGN;
+  }
+  {
+    const int64_t qb = q_bytes(s), kb = kv_bytes(s), sb = stat_bytes(s);
+    st = check_alias({span(dq, qb), span(dk, kb), span(dv, kb), span(workspace, (int64_t)need)},
+                     {span(q, qb), span(k, kb), span(v, kb), span(o, qb), span(dO, qb),
+                      span(row_max, sb), span(row_sum, sb)});
+    if (st != MEA_OK) return st;
   }
   mea::BwdProblem p;
   p.heads = s.heads;
@@ -206,6 +249,7 @@ const char* attn_status_str(mea_status_t s) {
     case MEA_ERR_ALIGN: return "MEA_ERR_ALIGN";
     case MEA_ERR_WORKSPACE: return "MEA_ERR_WORKSPACE";
     case MEA_ERR_LAUNCH: return "MEA_ERR_LAUNCH";
+    case MEA_ERR_ALIAS: return "MEA_ERR_ALIAS";
   }
   return "MEA_UNKNOWN_STATUS";
 }
@@ -288,6 +332,10 @@ mea_status_t attn_fwd_splitkv(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv
     if (workspace == nullptr || workspace_bytes < need) return MEA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MEA_ERR_ALIGN;
   }
+  st = check_alias({span(o, q_bytes(s)), span(row_max, stat_bytes(s)), span(row_sum, stat_bytes(s)),
+                    span(workspace, (int64_t)need)},
+                   {span(q, q_bytes(s)), span(k, kv_bytes(s)), span(v, kv_bytes(s))});
+  if (st != MEA_OK) return st;
   hipStream_t stream_h = reinterpret_cast<hipStream_t>(stream);
   mea::FwdProblem p = fwd_problem(s, q, k, v, o, row_max, row_sum);
   if (plan.splits > 1) {

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mea.h")
 
 F32, BF16 = mea.DTYPE_F32, mea.DTYPE_BF16
-OK, NULL, SHAPE, UNSUP, ALIGN, WS, LAUNCH = range(7)
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, LAUNCH, ALIAS = range(8)
 A = 0x10000  # aligned fake device addresses: validation never dereferences them
 
 
@@ -59,10 +59,11 @@ def test_exports_nothing_but_the_c_abi():
 
 def test_status_strings(L):
     for code, name in enumerate(["MEA_OK", "MEA_ERR_NULL", "MEA_ERR_SHAPE", "MEA_ERR_UNSUPPORTED",
-                                 "MEA_ERR_ALIGN", "MEA_ERR_WORKSPACE", "MEA_ERR_LAUNCH"]):
+                                 "MEA_ERR_ALIGN", "MEA_ERR_WORKSPACE", "MEA_ERR_LAUNCH",
+                                 "MEA_ERR_ALIAS"]):
         assert mea.attn_status_str(code) == name
     assert mea.attn_status_str(99) == "MEA_UNKNOWN_STATUS"
-    assert mea.mea_version() == 200
+    assert mea.mea_version() == 300
 
 
 def fwd(L, dt=BF16, B=1, H=1, n=128, d=64, q=A, k=A, v=A, o=A, m=0, l=0):
@@ -118,6 +119,43 @@ def test_bwd_validation(L):
     assert bwd(L, wsb=8 * 128 - 1) == WS
     assert bwd(L, wsb=8 * 128, ws=A + 8) == ALIGN
     assert bwd(L, B=0, ws=0, wsb=0, ptrs={k: 0 for k in ("q", "k", "v")}) == OK
+
+
+# distinct fake buffers 1 MiB apart (every tensor below is far smaller)
+Q, K, V, O, M, LS, DO, DQ, DK, DV, W = (A + (i << 20) for i in range(11))
+
+
+def test_outputs_must_not_overlap(L):
+    # n = 128, d = 64, bf16: q-side tensors 16 KiB, statistics 512 B, workspace 1 KiB.
+    # Every call below stops at the overlap check (a passing call would launch).
+    qb = 128 * 64 * 2
+    f = lambda **kw: fwd(L, **dict(dict(q=Q, k=K, v=V, o=O, m=M, l=LS), **kw))
+    assert f(o=Q) == ALIAS                      # in place
+    assert f(o=Q + qb - 16) == ALIAS            # last 16 bytes shared
+    assert f(o=V - qb + 16) == ALIAS
+    assert f(m=O + qb - 16) == ALIAS            # statistics inside the output
+    assert f(l=M) == ALIAS
+    assert f(l=M + 512 - 16) == ALIAS
+    b = lambda ws=W, **kw: bwd(L, ws=ws, wsb=1 << 20, ptrs=dict(
+        dict(q=Q, k=K, v=V, o=O, do=DO, m=M, l=LS, dq=DQ, dk=DK, dv=DV), **kw))
+    assert b(dq=Q) == ALIAS
+    assert b(dq=DO) == ALIAS
+    assert b(dk=DV) == ALIAS
+    assert b(dv=K + qb - 16) == ALIAS
+    assert b(ws=DQ + qb - 16) == ALIAS          # the workspace is written too
+    assert b(ws=LS) == ALIAS
+    assert b(dk=M) == ALIAS
+    # without query rows only dk, dv and the key side remain
+    assert bwd_ex(L, n_q=0, ws=0, wsb=0, ptrs=dict(q=0, o=0, do=0, m=0, l=0, dq=0,
+                                                   k=K, v=V, dk=K, dv=DV)) == ALIAS
+    # split-key: 16384 keys make K and V 2 MiB each, so these buffers sit 16 MiB apart
+    sq, sk, sv, so, sm, sl, sw = (A + (i << 24) for i in range(7))
+    need = mea.attn_fwd_splitkv_workspace_bytes(BF16, 1, 1, 1, 1, 16384, 64, 0)
+    sp = lambda **kw: split(L, **dict(dict(q=sq, k=sk, v=sv, o=so, m=sm, l=sl, ws=sw, wsb=need), **kw))
+    assert sp(ws=so) == ALIAS
+    assert sp(ws=sl - need + 16) == ALIAS
+    assert sp(ws=sk + (2 << 20) - 16) == ALIAS
+    assert sp(o=sv + (2 << 20) - 16) == ALIAS
 
 
 def test_workspace_bytes(L):
@@ -285,7 +323,7 @@ int main(void) {
   char buf[16] __attribute__((aligned(16)));
   void* p = buf;
   /* validation paths only: no call below reaches a kernel launch */
-  if (mea_version() != 200) return 1;
+  if (mea_version() != 300) return 1;
   if (attn_fwd(MEA_DTYPE_BF16, 1, 1, 8, 96, p, p, p, p, NULL, NULL, NULL) != MEA_ERR_UNSUPPORTED) return 2;
   if (attn_fwd_ex(MEA_DTYPE_F32, 1, 4, 3, 8, 8, 64, p, p, p, p, NULL, NULL, NULL) != MEA_ERR_SHAPE) return 3;
   if (attn_bwd(MEA_DTYPE_BF16, 0, 1, 8, 64, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
