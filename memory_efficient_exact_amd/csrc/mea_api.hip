@@ -128,7 +128,7 @@ SplitPlan plan_splits(const Shape& s, int64_t requested) {
   SplitPlan p;
   p.split_len = s.n_k;
   if (s.empty || s.n_k == 0) return p;
-  const mea::FwdGeometry g = mea::fwd_geometry(s.bf16, s.d, s.rows_q);
+  const mea::FwdGeometry g = mea::fwd_geometry(s.bf16, s.d, s.heads, s.rows_q);
   const int64_t tiles_k = cdiv(s.n_k, g.key_tile);
   int64_t want = requested;
   if (want <= 0) {
@@ -325,7 +325,8 @@ mea_status_t attn_fwd_splitkv(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv
   if (st != MEA_OK) return st;
   if (row_max != nullptr && (!aligned16(row_max) || !aligned16(row_sum))) return MEA_ERR_ALIGN;
   const SplitPlan plan = plan_splits(s, num_splits);
-  if (s.heads * plan.splits * cdiv(s.rows_q, mea::fwd_geometry(s.bf16, s.d, s.rows_q).query_rows) > kMaxBlocks)
+  if (s.heads * plan.splits * cdiv(s.rows_q, mea::fwd_geometry(s.bf16, s.d, s.heads, s.rows_q).query_rows) >
+      kMaxBlocks)
     return MEA_ERR_SHAPE;
   const size_t need = split_workspace_bytes(s, plan);
   if (need > 0) {

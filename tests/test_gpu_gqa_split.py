@@ -213,3 +213,30 @@ def test_splitkv_bf16_large_scores():
     check("O split", f64(o.cpu()), o_ref, "bf16")
     check("O unsplit", f64(o1.cpu()), o_ref, "bf16")
     check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, "bf16")
+
+
+# ------------------------------------------------------- 8-wave forward workgroups
+# The bf16 forward takes 8-wave workgroups (512 query rows at d = 64, 256 at
+# d = 128) when heads x tiles of that size reach 256; these shapes do, with a
+# ragged last tile, grouped heads and key counts that are not tile multiples.
+WIDE_CASES = [(1, 256, 256, 600, 300, 64), (2, 256, 64, 150, 200, 64),
+              (1, 128, 128, 300, 333, 128), (4, 256, 32, 40, 97, 128)]
+
+
+@pytest.mark.parametrize("B,H,H_kv,n_q,n_k,d", WIDE_CASES)
+@pytest.mark.parametrize("splits", [None, 3])
+def test_wide_workgroups_full(B, H, H_kv, n_q, n_k, d, splits):
+    rows = (512 if d == 64 else 256)
+    assert B * H_kv * -(-(H // H_kv) * n_q // rows) >= 256  # the 8-wave layout is taken
+    say("wide", B, H, H_kv, n_q, n_k, d, splits)
+    t = draw(B, H, H_kv, n_q, n_k, d, "bf16", seed=151 + n_q + d)
+    q, k, v = (gpu(t[x]) for x in ("q", "k", "v"))
+    if splits is None:
+        o, m, l = mea.attn_fwd_ex(q, k, v)
+    else:
+        assert mea.attn_fwd_splitkv_num_splits(mea.DTYPE_BF16, B, H, H_kv, n_q, n_k, d, splits) > 1
+        o, m, l = mea.attn_fwd_splitkv(q, k, v, num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, m_ref, l_ref = oracle.gqa_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]))
+    check("O", f64(o.cpu()), o_ref, "bf16")
+    check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, "bf16")
