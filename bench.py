@@ -360,13 +360,13 @@ def main():
     log(f"step {ms:.3f} ms | fwd {f_avg:.3f} ms ({fwd_tf:.1f} TFLOP/s, "
         f"{100 * fwd_tf / PEAK_BF16_TFLOPS:.1f}% of peak) | bwd {b_avg:.3f} ms ({bwd_tf:.1f} TFLOP/s)")
 
-    # Roofline of the dominant kernel, bwd_main_kernel<64> (the backward's
+    # Roofline of the dominant kernel, bwd_main_kernel<64, 8> (the backward's
     # MFMA work: algorithmically 10*B*H*n^2*d flops per launch). Its average
     # launch duration is taken from HIP events around each attn_bwd call on the
     # launch stream; that call also runs the O(n*d) row pass (a few
     # microseconds), so the figure is a slight underestimate.
     roofline = {
-        "kernel": "bwd_main_kernel<64>",
+        "kernel": "bwd_main_kernel<64, 8>",
         "bound": "mfma",
         "achieved": bwd_tf,
         "peak": PEAK_BF16_TFLOPS,

@@ -240,3 +240,25 @@ def test_wide_workgroups_full(B, H, H_kv, n_q, n_k, d, splits):
     o_ref, m_ref, l_ref = oracle.gqa_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]))
     check("O", f64(o.cpu()), o_ref, "bf16")
     check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, "bf16")
+
+
+# The bf16 backward at d = 64 takes 8-wave workgroups (256 keys or queries each)
+# when heads x (key tiles + query tiles) of that size reach 256: ragged tiles on both
+# sides, grouped heads, and fewer keys than one workgroup covers.
+WIDE_BWD_CASES = [(1, 128, 128, 300, 300), (4, 64, 16, 70, 300), (1, 64, 64, 1000, 77)]
+
+
+@pytest.mark.parametrize("B,H,H_kv,n_q,n_k", WIDE_BWD_CASES)
+def test_wide_workgroups_backward_full(B, H, H_kv, n_q, n_k):
+    rows_q = (H // H_kv) * n_q
+    assert B * H_kv * (-(-n_k // 256) - (-rows_q // 256)) >= 256  # the 8-wave layout is taken
+    say("wide bwd", B, H, H_kv, n_q, n_k)
+    t = draw(B, H, H_kv, n_q, n_k, 64, "bf16", seed=161 + n_q, with_do=True)
+    q, k, v, do = (gpu(t[x]) for x in ("q", "k", "v", "do"))
+    o, m, l = mea.attn_fwd_ex(q, k, v)
+    dq, dk, dv = mea.attn_bwd_ex(q, k, v, o, do, m, l)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.gqa_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]))
+    check("dQ", f64(dq.cpu()), rq, "bf16")
+    check("dK", f64(dk.cpu()), rk, "bf16")
+    check("dV", f64(dv.cpu()), rv, "bf16")
