@@ -121,37 +121,46 @@ def _dtype_code(t):
     raise ValueError(f"unsupported dtype {t.dtype}; expected torch.bfloat16 or torch.float32")
 
 
-def _check(name, t, like):
+# The checks below run on every call, so each takes one combined test on the
+# common path and builds its message only when the test fails.
+
+def _check_as(name, t, shape, like, dev=None):
+    """t must be a contiguous GPU tensor of `shape` with like's dtype and device
+    (`dev`: like's device index, when the caller has it already)."""
+    if dev is None:
+        dev = like.get_device()
+    if dev >= 0 and t.get_device() == dev and t.shape == shape and t.dtype == like.dtype \
+            and t.is_contiguous():
+        return
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     if t.device != like.device:
         raise ValueError(f"{name} is on {t.device}, expected {like.device}")
-    if tuple(t.shape) != tuple(like.shape) or t.dtype != like.dtype:
-        raise ValueError(f"{name} must match q: shape {tuple(like.shape)} dtype {like.dtype}, "
+    if tuple(t.shape) != tuple(shape) or t.dtype != like.dtype:
+        raise ValueError(f"{name} must have shape {tuple(shape)} dtype {like.dtype}, "
                          f"got {tuple(t.shape)} {t.dtype}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+    raise ValueError(f"{name} must be contiguous")
 
 
-def _check_stat(name, t, q):
+def _check(name, t, like, dev=None):
+    _check_as(name, t, like.shape, like, dev)
+
+
+def _check_stat(name, t, q, dev=None, rows=None):
+    """t must be a contiguous float32 GPU tensor of shape q.shape[:3] on q's device."""
+    import torch
+    if dev is None:
+        dev = q.get_device()
+    if rows is None:
+        rows = q.shape[:3]
+    if dev >= 0 and t.get_device() == dev and t.shape == rows and t.dtype == torch.float32 \
+            and t.is_contiguous():
+        return
     if not t.is_cuda or t.device != q.device:
         raise ValueError(f"{name} must be on {q.device}")
     if tuple(t.shape) != tuple(q.shape[:3]):
         raise ValueError(f"{name} must have shape {tuple(q.shape[:3])}, got {tuple(t.shape)}")
-    import torch
-    if t.dtype != torch.float32 or not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous float32")
-
-
-def _check_as(name, t, shape, like):
-    """t must be a contiguous GPU tensor of `shape` with like's dtype and device."""
-    if not t.is_cuda or t.device != like.device:
-        raise ValueError(f"{name} must be a GPU tensor on {like.device}")
-    if tuple(t.shape) != tuple(shape) or t.dtype != like.dtype:
-        raise ValueError(f"{name} must have shape {tuple(shape)} dtype {like.dtype}, "
-                         f"got {tuple(t.shape)} {t.dtype}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+    raise ValueError(f"{name} must be contiguous float32")
 
 
 def _gqa_shapes(q, k, v):
@@ -160,9 +169,11 @@ def _gqa_shapes(q, k, v):
         raise ValueError("q must be [B, H, n_q, d] and k, v [B, H_kv, n_k, d]")
     B, H, n_q, d = q.shape
     H_kv, n_k = k.shape[1], k.shape[2]
-    _check_as("q", q, q.shape, q)
-    _check_as("k", k, (B, H_kv, n_k, d), q)
-    _check_as("v", v, (B, H_kv, n_k, d), q)
+    di = q.get_device()
+    _check_as("q", q, q.shape, q, di)
+    kv = (B, H_kv, n_k, d)
+    _check_as("k", k, kv, q, di)
+    _check_as("v", v, kv, q, di)
     return B, H, H_kv, n_q, n_k, d
 
 
@@ -177,8 +188,9 @@ def _fwd_outputs(q, out, row_max, row_sum, stats):
         row_max = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
         row_sum = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     if row_max is not None:
-        _check_stat("row_max", row_max, q)
-        _check_stat("row_sum", row_sum, q)
+        di, rows = q.get_device(), q.shape[:3]
+        _check_stat("row_max", row_max, q, di, rows)
+        _check_stat("row_sum", row_sum, q, di, rows)
     return out, row_max, row_sum
 
 
@@ -192,14 +204,28 @@ def _workspace(workspace, need, device):
 
 
 def _stream(stream, device):
+    """Raw hipStream_t of `stream`, or of torch's current stream on `device`."""
+    if stream is not None:
+        return stream.cuda_stream
     import torch
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream)
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+    return t.data_ptr() if t is not None else None
+
+
+def _call(device, fn, *args):
+    """Call a library entry point with `device` current (the kernels launch on
+    the current HIP device); the device switch is skipped when it already is."""
+    import torch
+    if torch.cuda.current_device() == device.index:
+        return fn(*args)
+    with torch.cuda.device(device):
+        return fn(*args)
 
 
 def attn_fwd(q, k, v, out=None, row_max=None, row_sum=None, stats=True, stream=None):
@@ -213,24 +239,26 @@ def attn_fwd(q, k, v, out=None, row_max=None, row_sum=None, stats=True, stream=N
     if q.dim() != 4:
         raise ValueError("q must be [B, H, n, d]")
     dt = _dtype_code(q)
-    _check("q", q, q)
-    _check("k", k, q)
-    _check("v", v, q)
+    di = q.get_device()
+    _check("q", q, q, di)
+    _check("k", k, q, di)
+    _check("v", v, q, di)
     if out is None:
         out = torch.empty_like(q)
-    _check("out", out, q)
+    _check("out", out, q, di)
     if (row_max is None) != (row_sum is None):
         raise ValueError("pass both row_max and row_sum, or neither")
     if row_max is None and stats:
         row_max = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
         row_sum = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     if row_max is not None:
-        _check_stat("row_max", row_max, q)
-        _check_stat("row_sum", row_sum, q)
+        rows = q.shape[:3]
+        _check_stat("row_max", row_max, q, di, rows)
+        _check_stat("row_sum", row_sum, q, di, rows)
     B, H, n, d = q.shape
-    with torch.cuda.device(q.device):
-        st = lib().attn_fwd(dt, B, H, n, d, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
-                            _ptr(row_max), _ptr(row_sum), _stream(stream, q.device))
+    dev = q.device
+    st = _call(dev, lib().attn_fwd, dt, B, H, n, d, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+               _ptr(row_max), _ptr(row_sum), _stream(stream, dev))
     if st != 0:
         raise MeaError("attn_fwd", st)
     return out, row_max, row_sum
@@ -246,15 +274,17 @@ def attn_bwd(q, k, v, o, do, row_max, row_sum, dq=None, dk=None, dv=None, worksp
     if q.dim() != 4:
         raise ValueError("q must be [B, H, n, d]")
     dt = _dtype_code(q)
+    di = q.get_device()
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
-        _check(name, t, q)
-    _check_stat("row_max", row_max, q)
-    _check_stat("row_sum", row_sum, q)
+        _check(name, t, q, di)
+    rows = q.shape[:3]
+    _check_stat("row_max", row_max, q, di, rows)
+    _check_stat("row_sum", row_sum, q, di, rows)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _check(name, t, q)
+        _check(name, t, q, di)
     B, H, n, d = q.shape
     need = attn_bwd_workspace_bytes(dt, B, H, n, d)
     if workspace is None:
@@ -262,10 +292,10 @@ def attn_bwd(q, k, v, o, do, row_max, row_sum, dq=None, dk=None, dv=None, worksp
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
     wbytes = workspace.numel() * workspace.element_size()
-    with torch.cuda.device(q.device):
-        st = lib().attn_bwd(dt, B, H, n, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
-                            _ptr(row_max), _ptr(row_sum), _ptr(dq), _ptr(dk), _ptr(dv),
-                            _ptr(workspace), wbytes, _stream(stream, q.device))
+    dev = q.device
+    st = _call(dev, lib().attn_bwd, dt, B, H, n, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+               _ptr(row_max), _ptr(row_sum), _ptr(dq), _ptr(dk), _ptr(dv),
+               _ptr(workspace), wbytes, _stream(stream, dev))
     if st != 0:
         raise MeaError("attn_bwd", st)
     return dq, dk, dv
@@ -275,13 +305,12 @@ def attn_fwd_ex(q, k, v, out=None, row_max=None, row_sum=None, stats=True, strea
     """Forward with separate lengths and shared key/value heads: q [B, H, n_q, d],
     k and v [B, H_kv, n_k, d] with H a multiple of H_kv; query head h reads
     key/value head h // (H // H_kv). Returns (o, row_max, row_sum) as ``attn_fwd``."""
-    import torch
     dt = _dtype_code(q)
     B, H, H_kv, n_q, n_k, d = _gqa_shapes(q, k, v)
     out, row_max, row_sum = _fwd_outputs(q, out, row_max, row_sum, stats)
-    with torch.cuda.device(q.device):
-        st = lib().attn_fwd_ex(dt, B, H, H_kv, n_q, n_k, d, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
-                               _ptr(row_max), _ptr(row_sum), _stream(stream, q.device))
+    dev = q.device
+    st = _call(dev, lib().attn_fwd_ex, dt, B, H, H_kv, n_q, n_k, d, _ptr(q), _ptr(k), _ptr(v),
+               _ptr(out), _ptr(row_max), _ptr(row_sum), _stream(stream, dev))
     if st != 0:
         raise MeaError("attn_fwd_ex", st)
     return out, row_max, row_sum
@@ -306,10 +335,10 @@ def attn_bwd_ex(q, k, v, o, do, row_max, row_sum, dq=None, dk=None, dv=None, wor
     _check_as("dv", dv, v.shape, q)
     workspace, wbytes = _workspace(workspace, attn_bwd_ex_workspace_bytes(dt, B, H, H_kv, n_q, n_k, d),
                                    q.device)
-    with torch.cuda.device(q.device):
-        st = lib().attn_bwd_ex(dt, B, H, H_kv, n_q, n_k, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                               _ptr(do), _ptr(row_max), _ptr(row_sum), _ptr(dq), _ptr(dk),
-                               _ptr(dv), _ptr(workspace), wbytes, _stream(stream, q.device))
+    dev = q.device
+    st = _call(dev, lib().attn_bwd_ex, dt, B, H, H_kv, n_q, n_k, d, _ptr(q), _ptr(k), _ptr(v),
+               _ptr(o), _ptr(do), _ptr(row_max), _ptr(row_sum), _ptr(dq), _ptr(dk), _ptr(dv),
+               _ptr(workspace), wbytes, _stream(stream, dev))
     if st != 0:
         raise MeaError("attn_bwd_ex", st)
     return dq, dk, dv
@@ -321,16 +350,15 @@ def attn_fwd_splitkv(q, k, v, num_splits=0, out=None, row_max=None, row_sum=None
     workgroups and merged afterwards (for small grids and decoding).
     ``num_splits`` 0 lets the library choose. ``workspace`` (a GPU tensor of at
     least ``attn_fwd_splitkv_workspace_bytes`` bytes) is allocated if not passed."""
-    import torch
     dt = _dtype_code(q)
     B, H, H_kv, n_q, n_k, d = _gqa_shapes(q, k, v)
     out, row_max, row_sum = _fwd_outputs(q, out, row_max, row_sum, stats)
     need = attn_fwd_splitkv_workspace_bytes(dt, B, H, H_kv, n_q, n_k, d, num_splits)
     workspace, wbytes = _workspace(workspace, need, q.device)
-    with torch.cuda.device(q.device):
-        st = lib().attn_fwd_splitkv(dt, B, H, H_kv, n_q, n_k, d, _ptr(q), _ptr(k), _ptr(v),
-                                    _ptr(out), _ptr(row_max), _ptr(row_sum), int(num_splits),
-                                    _ptr(workspace), wbytes, _stream(stream, q.device))
+    dev = q.device
+    st = _call(dev, lib().attn_fwd_splitkv, dt, B, H, H_kv, n_q, n_k, d, _ptr(q), _ptr(k),
+               _ptr(v), _ptr(out), _ptr(row_max), _ptr(row_sum), int(num_splits),
+               _ptr(workspace), wbytes, _stream(stream, dev))
     if st != 0:
         raise MeaError("attn_fwd_splitkv", st)
     return out, row_max, row_sum
