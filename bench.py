@@ -54,6 +54,39 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+MIN_WARM_S = 0.2    # warm-up wall time before a timed loop (the clock leaves its idle state)
+MIN_TIMED_S = 0.05  # least GPU time of a timed loop
+
+
+def timed_loop(fn, warmup, steps, dev):
+    """Average ms per call of `fn` over back-to-back calls between two HIP events:
+    at least `warmup` calls and MIN_WARM_S of warm-up first, then at least `steps`
+    calls and MIN_TIMED_S of GPU time. Short calls otherwise run partly at the
+    lower clock the GPU drops to while the host prepares inputs."""
+    import time
+
+    import torch
+    t0, i = time.perf_counter(), 0
+    while i < warmup or time.perf_counter() - t0 < MIN_WARM_S:
+        fn()
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize(dev)
+    count = steps
+    while True:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        e0.record()
+        for _ in range(count):
+            fn()
+        e1.record()
+        torch.cuda.synchronize(dev)
+        total = e0.elapsed_time(e1)
+        if total >= 1e3 * MIN_TIMED_S or count >= 1 << 16:
+            return total / count
+        count = max(count + 1, int(count * 1e3 * MIN_TIMED_S / max(total, 1e-3)) + 1)
+
+
 def cpu_baseline(w):
     """The fp64 oracle as it stands, on one of the workload's heads (all n
     query rows, forward then backward), timed on this host's cores."""
@@ -108,16 +141,7 @@ def sweep_configs(steps, warmup):
         torch.cuda.reset_peak_memory_stats(dev)
 
         def timed(fn):
-            for _ in range(warmup):
-                fn()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize(dev)
-            e0.record()
-            for _ in range(steps):
-                fn()
-            e1.record()
-            torch.cuda.synchronize(dev)
-            return e0.elapsed_time(e1) / steps
+            return timed_loop(fn, warmup, steps, dev)
 
         fms = timed(lambda: mea.attn_fwd(q, k, v, out=o, row_max=m, row_sum=l))
         row["fwd_ms"] = fms
@@ -141,7 +165,8 @@ def sweep_configs(steps, warmup):
         log(json.dumps(row))
         del t, q, k, v, do, o, m, l
         torch.cuda.empty_cache()
-    return {"mode": "configs", "steps": steps, "warmup": warmup, "rows": rows}
+    return {"mode": "configs", "steps": steps, "warmup": warmup, "min_warm_s": MIN_WARM_S,
+            "min_timed_s": MIN_TIMED_S, "rows": rows}
 
 
 # Shapes for the split-key / grouped-query sweep: (name, B, H, H_kv, n_q, n_k, d, dtype, backward).
@@ -182,16 +207,7 @@ def sweep_split(steps, warmup):
                          dtype=torch.uint8, device=dev)
 
         def timed(fn):
-            for _ in range(warmup):
-                fn()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize(dev)
-            e0.record()
-            for _ in range(steps):
-                fn()
-            e1.record()
-            torch.cuda.synchronize(dev)
-            return e0.elapsed_time(e1) / steps
+            return timed_loop(fn, warmup, steps, dev)
 
         flops = 4.0 * B * H * n_q * n_k * d
         esz = q.element_size()
@@ -220,7 +236,8 @@ def sweep_split(steps, warmup):
         log(json.dumps(row))
         del t, q, k, v, o, m, l, ws
         torch.cuda.empty_cache()
-    return {"mode": "splitkv", "steps": steps, "warmup": warmup, "rows": rows}
+    return {"mode": "splitkv", "steps": steps, "warmup": warmup, "min_warm_s": MIN_WARM_S,
+            "min_timed_s": MIN_TIMED_S, "rows": rows}
 
 
 def sweep_memory():
