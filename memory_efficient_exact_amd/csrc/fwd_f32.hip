@@ -11,9 +11,17 @@
 // the weights of near-tied keys by far more than the 1e-5 output tolerance.
 //
 // Work split: 4 waves, 16 query rows per wave; K/V tiles of 32 keys in LDS,
-// double-buffered, rows padded so the column reads of both MFMA operands hit
-// distinct banks. The score tile is transposed (lane = query), so the per-row
-// state lives in registers; four lanes (l, l^16, l^32, l^48) share a query.
+// rows padded so the column reads of both MFMA operands hit distinct banks.
+// The tile is single-buffered: after every wave is done with it, the next one
+// is loaded and stored between two barriers. The small LDS footprint and
+// register budget (Q held in fp32 and widened at each use) let three
+// workgroups share a CU at d = 128, four at d = 64, and the other workgroups
+// cover the load (measured 10% faster than double buffering with the next
+// tile held in registers, at two workgroups per CU). Decoding grids are too
+// small for that, so the decoding layout below keeps the double buffer with
+// the next tile loaded into registers during the current one. The score tile
+// is transposed (lane = query), so the per-row state lives in registers; four
+// lanes (l, l^16, l^32, l^48) share a query.
 //
 // Decoding mode (at most 32 query rows per head): the four waves share one
 // 16-row query block and each takes a different 16-key block of every 64-key
@@ -62,8 +70,9 @@ struct FwdArgs32 {
   double scale64;  // 1 / sqrt(D)
 };
 
+// at least three waves per SIMD (<= 168 registers) outside decoding
 template <int D, bool kDecode>
-__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs32 a) {
+__global__ __launch_bounds__(kThreads, kDecode ? 1 : 3) void fwd_f32_kernel(const FwdArgs32 a) {
   constexpr int KS = D + 4;   // K row stride (floats): 16-byte pad
   constexpr int VS = D + 16;  // V row stride (floats): 64-byte pad
   constexpr int KK = D / 4;   // k-steps of the fp64 score MFMA
@@ -75,8 +84,9 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs32 a) {
   constexpr int kLoads = BC * D / 4 / kThreads;
   static_assert(kLoads * 4 * kThreads == BC * D, "tile split");
 
-  __shared__ __attribute__((aligned(16))) float sK[2][BC * KS];
-  __shared__ __attribute__((aligned(16))) float sV[2][BC * VS];
+  constexpr int NB = kDecode ? 2 : 1;  // LDS buffers per operand
+  __shared__ __attribute__((aligned(16))) float sK[NB][BC * KS];
+  __shared__ __attribute__((aligned(16))) float sV[NB][BC * VS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -100,11 +110,11 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs32 a) {
   const int blk0 = kDecode ? wave : 0;  // first 16-key block of a tile this wave takes
   const int64_t grow = (int64_t)bh * n_q + row;
 
-  // B operand of S^T = K Q^T: Q[row][4*kk + g4] as fp64
-  double qd[KK];
+  // B operand of S^T = K Q^T: Q[row][4*kk + g4], widened to fp64 (exactly) at each use
+  float qf[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
-    qd[kk] = row < n_q ? (double)a.Q[grow * D + 4 * kk + g4] : 0.0;
+    qf[kk] = row < n_q ? a.Q[grow * D + 4 * kk + g4] : 0.f;
 
   double m_run = -INFINITY;  // running max of raw scores (fp64)
   float l_run = 0.f;         // this lane's share of the running sum
@@ -146,9 +156,11 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs32 a) {
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+    const int buf = NB == 2 ? (t & 1) : 0;
     const int j0 = t * BC;
-    if (t + 1 < ntiles) gload(j0 + BC);
+    if constexpr (NB == 2) {
+      if (t + 1 < ntiles) gload(j0 + BC);
+    }
     const float* ks = sK[buf];
     const float* vs = sV[buf];
 
@@ -160,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs32 a) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const double a = (double)ks[((blk0 + kb) * 16 + l16) * KS + 4 * kk + g4];
-        s[kb] = mfma_f64_16x16x4(a, qd[kk], s[kb]);
+        s[kb] = mfma_f64_16x16x4(a, (double)qf[kk], s[kb]);
       }
     }
     if (j0 + BC > n) {
@@ -208,7 +220,13 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs32 a) {
         for (int db = 0; db < DB; ++db) acc[db] = mfma_f32_16x16x4(vrow[db * 16], p[kb][c], acc[db]);
       }
 
-    if (t + 1 < ntiles) swrite(buf ^ 1);
+    if constexpr (NB == 2) {
+      if (t + 1 < ntiles) swrite(buf ^ 1);
+    } else if (t + 1 < ntiles) {
+      __syncthreads();  // every wave is done with this tile
+      gload(j0 + BC);
+      swrite(0);
+    }
     __syncthreads();
   }
 
@@ -221,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const FwdArgs32 a) {
     // with a barrier, so the tile buffers are free: per-wave maxima and sums go
     // to sK[0], each wave's re-based accumulator (16 rows x D) to sV[0].
     constexpr int AS = D + 4;
-    static_assert(kWaves * 16 * AS <= BC * VS, "accumulators fit one V buffer");
+    static_assert(kWaves * 16 * AS <= BC * VS, "accumulators fit the V buffer");
     double* sm = reinterpret_cast<double*>(sK[0]);
     float* sl = sK[0] + 2 * kWaves * 16;
     float* sacc = sV[0];
@@ -339,9 +357,11 @@ hipError_t launch(const FwdProblem& p, hipStream_t stream) {
 }  // namespace
 
 FwdGeometry fwd_geometry_f32(int d, int64_t rows_q) {
-  // decoding at d = 128 double-buffers 64-key tiles in 141 KiB of LDS: one workgroup per CU
+  // workgroups per CU: decoding double-buffers 64-key tiles (at d = 128 in 141 KiB
+  // of LDS, one workgroup per CU); otherwise as the register budgets allow, four
+  // at d = 64 and three at d = 128
   if (rows_q <= kDecodeRows) return FwdGeometry{kBQDecode, kBCDecode, d == 64 ? 2 : 1};
-  return FwdGeometry{kBQ, kBC, 2};
+  return FwdGeometry{kBQ, kBC, d == 64 ? 4 : 3};
 }
 
 hipError_t launch_fwd_f32(int d, const FwdProblem& p, hipStream_t stream) {
