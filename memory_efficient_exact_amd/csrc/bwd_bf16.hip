@@ -14,18 +14,22 @@
 // Two launches on the caller's stream:
 //  1. bwd_rows: -D_i and lse2_i for every row, into the workspace (reads O,
 //     dO, m, l once; a few microseconds).
-//  2. bwd_main: one grid holding two kinds of workgroup of W waves (W = 8,
-//     one workgroup per CU, at d = 64 when that grid covers every CU; else
-//     W = 4: two per CU at d = 64, one at d = 128).
-//     * dK/dV workgroups own 32*W keys (32 per wave, K and V of those keys in
+//  2. bwd_main: one grid holding two kinds of workgroup of W waves, two waves
+//     per SIMD: W = 8 (one workgroup per CU) when that grid covers every CU,
+//     else W = 4 (two per CU).
+//     * dK/dV workgroups own R*W keys (R per wave, K and V of those keys in
 //       registers) and sweep every query tile of 64 rows (Q, dO, lse2, D
 //       copied into LDS by DMA, double-buffered), accumulating dV^T and dK^T
 //       in registers: per tile S = Q K^T, dP = dO V^T (lane = key), then
 //       dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T from transposed LDS
 //       reads.
-//     * dQ workgroups own 32*W queries (32 per wave, Q and dO in registers)
+//     * dQ workgroups own R*W queries (R per wave, Q and dO in registers)
 //       and sweep every key tile of 64 keys (K, V in LDS), accumulating dQ^T:
 //       S^T = K Q^T, dP^T = V dO^T (lane = query), dQ^T += K^T dS^T.
+//     d = 64 takes R = 32 rows per wave on 32x32x16 MFMAs and padded LDS
+//     tiles (bwd_main_kernel); d = 128 takes R = 16 on 16x16x32 MFMAs and
+//     swizzled tiles (bwd_main128_kernel), which halves the accumulators so
+//     that two waves still fit per SIMD.
 //     The dK/dV workgroups come first in the grid (they carry more work), the
 //     dQ workgroups fill the machine behind them.
 // No probability or score array is written to memory; dQ, dK and dV are each
@@ -44,8 +48,8 @@ namespace mea {
 namespace {
 
 constexpr int kThreads = 256;     // row-term kernel
-constexpr int kWaves = 4;         // waves per main-kernel workgroup: d = 128 and small grids
-constexpr int kWideWaves = 8;     // d = 64 on grids that fill the chip
+constexpr int kWaves = 4;         // waves per main-kernel workgroup on small grids
+constexpr int kWideWaves = 8;     // waves per main-kernel workgroup on grids that fill the chip
 constexpr int64_t kComputeUnits = 256;
 constexpr int kTileQ = 64;            // query rows per staged tile (dK/dV role)
 constexpr int kTileK = 64;            // key rows per staged tile (dQ role)
@@ -366,11 +370,11 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int wg, bf16* s0, bf16
   }
 }
 
-// d = 64 runs two waves per SIMD (<= 256 registers): 8-wave workgroups one per
-// CU, or 4-wave workgroups two per CU; d = 128 needs the full register file of
-// one wave per SIMD (4-wave workgroups, one per CU).
+// two waves per SIMD (<= 256 registers): 8-wave workgroups one per CU, or
+// 4-wave workgroups two per CU (d = 64; d = 128 has its own kernel above)
 template <int D, int W>
-__global__ __launch_bounds__(64 * W, D == 64 ? 2 : 1) void bwd_main_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * W, 2) void bwd_main_kernel(BwdArgs a) {
+  static_assert(D == 64, "d = 128 uses bwd_main128_kernel");
   // two named buffers per staged operand (see the forward kernel)
   __shared__ __attribute__((aligned(1024))) bf16 s0[BwdShared<D>::kElems];
   __shared__ __attribute__((aligned(1024))) bf16 s1[BwdShared<D>::kElems];
@@ -381,6 +385,320 @@ __global__ __launch_bounds__(64 * W, D == 64 ? 2 : 1) void bwd_main_kernel(BwdAr
   const int wg = blockIdx.x;
   if (wg < a.total_kv) dkdv_role<D, W>(a, wg, s0, s1, s2, s3, f0, f1);
   else dq_role<D, W>(a, wg - a.total_kv, s0, s1, s2, s3);
+}
+
+// ------------------------------------------------------------ d = 128 roles
+// 16 keys (dK/dV) or 16 queries (dQ) per wave on v_mfma_f32_16x16x32_bf16:
+//   A: lane l holds A[l%16][8*(l/16) + e];  B: lane l holds B[8*(l/16) + e][l%16]
+//   D: lane l, register r holds D[4*(l/16) + r][l%16]
+// A wave's dV^T and dK^T (or dQ^T) for 16 rows take 64 (32) registers instead
+// of 128 (64), so two waves fit per SIMD. Tiles are staged in the swizzled layout
+// (Swizzled<128>), where the 16-byte row reads of 16 lanes and the transposed
+// reads of 32 lanes used below each touch every bank once.
+//
+// The products dV^T += dO^T P and dK^T += Q^T dS contract over 32 query rows per
+// MFMA; their k index 8*(l/16) + e stands for row 4*(l/16) + e (e < 4) or
+// 16 + 4*(l/16) + e - 4 (e >= 4) of the 32-row chunk, which is the order in which
+// a lane holds P and dS from two 16-row score blocks, and the order in which two
+// transposed reads of 4 rows each deliver dO^T and Q^T.
+
+template <int ROWS, int WAVES>
+struct SwzDma128 {
+  using L = Swizzled<128>;
+  static constexpr int kBlocks = ROWS * L::kChunks / 64;
+  static constexpr int kPerWave = (kBlocks + WAVES - 1) / WAVES;
+  static_assert(kBlocks * 64 == ROWS * L::kChunks, "tile must be whole DMA blocks");
+  static constexpr int kElems = ROWS * 128;
+  int row[kPerWave];
+  int col[kPerWave];
+  int wave;
+  __device__ void init(int wave_, int lane) {
+    wave = wave_;
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int slot = (wave + WAVES * i) * 64 + lane;
+      const int r = slot / L::kChunks;
+      const int pc = slot - r * L::kChunks;
+      row[i] = r;
+      col[i] = (pc ^ L::swz(r)) * 8;
+    }
+  }
+  // rows r0 .. r0+ROWS-1 of src (row stride 128) into dst; rows past n repeat row n-1
+  __device__ void issue(const bf16* src, int r0, int n, bf16* dst) const {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int b = wave + WAVES * i;
+      if (b < kBlocks) {
+        const int sr = min(r0 + row[i], n - 1);
+        dma16(src + (int64_t)sr * 128 + col[i], dst + b * 512);
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int W>
+__device__ __forceinline__ void dkdv_role128(const BwdArgs& a, int wg, bf16* s0, bf16* s1,
+                                             bf16* s2, bf16* s3, float* f0, float* f1) {
+  constexpr int D = 128;
+  using L = Swizzled<D>;
+  using TQ = SwzDma128<kTileQ, W>;
+  constexpr int DK = D / 32;        // k-steps of the score products
+  constexpr int DB = D / 16;        // 16-row blocks of dV^T, dK^T
+  constexpr int QB = kTileQ / 16;   // 16-row score blocks per tile
+  constexpr int NC = kTileQ / 32;   // 32-row chunks (k-steps of dV, dK products)
+
+  const int n_q = a.n_q, n_k = a.n_k;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int tile = xcd_remap(wg, a.total_kv);
+  const int bh = tile / a.tiles_kv;
+  const int kt = tile - bh * a.tiles_kv;
+  const int64_t qbase = (int64_t)bh * n_q * D;
+  const int64_t kbase = (int64_t)bh * n_k * D;
+  const int64_t rbase = (int64_t)bh * n_q;
+  const int key = kt * (16 * W) + wave * 16 + l16;  // this lane's key (column of S)
+
+  // K and V of this wave's 16 keys: B operands of S = Q K^T and dP = dO V^T
+  bf16x8 kf[DK], vf[DK];
+  const int krow = min(key, n_k - 1);
+#pragma unroll
+  for (int dk = 0; dk < DK; ++dk) {
+    kf[dk] = *reinterpret_cast<const bf16x8*>(a.K + kbase + (int64_t)krow * D + dk * 32 + 8 * g);
+    vf[dk] = *reinterpret_cast<const bf16x8*>(a.V + kbase + (int64_t)krow * D + dk * 32 + 8 * g);
+  }
+  f32x4 accV[DB], accK[DB];  // dV^T, dK^T: register r of block db -> column 16*db + 4*g + r
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    accV[db] = f32x4{};
+    accK[db] = f32x4{};
+  }
+
+  TQ dma;
+  dma.init(wave, lane);
+  auto issue = [&](bf16* qdst, bf16* odst, float* fdst, int i0) {
+    dma.issue(a.Q + qbase, i0, n_q, qdst);
+    dma.issue(a.dO + qbase, i0, n_q, odst);
+    if (wave == W - 1) {
+      const int r = min(i0 + lane, n_q - 1);
+      dma4(a.Lse2 + rbase + r, fdst);
+      dma4(a.Dv + rbase + r, fdst + kTileQ);
+    }
+  };
+
+  // per-lane element offsets (row blocks of 16 rows keep the swizzle):
+  // row reads of row l16, columns 32*dk + 8*g; transposed reads of rows
+  // 4*g + l16/4 (and 16 below), columns 16*db + 4*(l16%4)
+  int a_off[DK], t_off[DB];
+#pragma unroll
+  for (int dk = 0; dk < DK; ++dk) a_off[dk] = L::off(l16, dk * 32 + 8 * g);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) t_off[db] = L::off(4 * g + (l16 >> 2), db * 16 + 4 * (l16 & 3));
+
+  auto tile_body = [&](const bf16* qs, const bf16* os, const float* fs, int i0, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      bf16x8 pf, sf;  // P and dS of query rows 32c + {4g .. 4g+3, 16+4g .. 16+4g+3}
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int qb = 2 * c + h;
+        // lane holds key `key`; register r holds query row i0 + 16*qb + 4*g + r.
+        // The dP accumulator starts at -D of its row, so it ends at dP - D.
+        f32x4 s = f32x4{};
+        f32x4 dp = *reinterpret_cast<const f32x4*>(fs + kTileQ + qb * 16 + 4 * g);
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) {
+          const int off = a_off[dk] + qb * 16 * D;
+          s = mfma16x16x32(lds_read_b128(qs + off), kf[dk], s);
+          dp = mfma16x16x32(lds_read_b128(os + off), vf[dk], dp);
+        }
+        const f32x4 lse = *reinterpret_cast<const f32x4*>(fs + qb * 16 + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float p = fast_exp2(__builtin_fmaf(s[r], a.C, -lse[r]));
+          if constexpr (kMasked) {
+            if (i0 + qb * 16 + 4 * g + r >= n_q) p = 0.f;  // padding query rows
+          }
+          pf[4 * h + r] = (bf16)p;
+          sf[4 * h + r] = (bf16)(p * dp[r]);
+        }
+      }
+      // dV^T += dO^T P,  dK^T += Q^T dS over the 32 rows of chunk c
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int o0 = t_off[db] + c * 32 * D, o1 = o0 + 16 * D;
+        const bf16x8 ao = cat(lds_read_tr16(os + o0), lds_read_tr16(os + o1));
+        const bf16x8 aq = cat(lds_read_tr16(qs + o0), lds_read_tr16(qs + o1));
+        accV[db] = mfma16x16x32(ao, pf, accV[db]);
+        accK[db] = mfma16x16x32(aq, sf, accK[db]);
+      }
+    }
+  };
+
+  const int ntiles = (n_q + kTileQ - 1) / kTileQ;
+  auto step = [&](const bf16* qs, const bf16* os, const float* fs, bf16* qn, bf16* on, float* fn,
+                  int t) {
+    const int i0 = t * kTileQ;
+    if (t + 1 < ntiles) issue(qn, on, fn, i0 + kTileQ);
+    if (i0 + kTileQ <= n_q) tile_body(qs, os, fs, i0, std::false_type{});
+    else tile_body(qs, os, fs, i0, std::true_type{});
+    wait_all();
+    __syncthreads();
+  };
+  if (ntiles > 0) {  // no query rows at all: dK = dV = 0
+    issue(s0, s1, f0, 0);
+    wait_all();
+    __syncthreads();
+  }
+  for (int t = 0; t < ntiles; t += 2) {
+    step(s0, s1, f0, s2, s3, f1, t);
+    if (t + 1 < ntiles) step(s2, s3, f1, s0, s1, f0, t + 1);
+  }
+
+  if (key < n_k) {
+    bf16* vrow = a.dV + kbase + (int64_t)key * D;
+    bf16* krow_out = a.dK + kbase + (int64_t)key * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      bf16x4 wv, wk;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        wv[r] = (bf16)accV[db][r];
+        wk[r] = (bf16)(accK[db][r] * a.scale);
+      }
+      *reinterpret_cast<bf16x4*>(vrow + db * 16 + 4 * g) = wv;
+      *reinterpret_cast<bf16x4*>(krow_out + db * 16 + 4 * g) = wk;
+    }
+  }
+}
+
+template <int W>
+__device__ __forceinline__ void dq_role128(const BwdArgs& a, int wg, bf16* s0, bf16* s1, bf16* s2,
+                                           bf16* s3) {
+  constexpr int D = 128;
+  using L = Swizzled<D>;
+  using TK = SwzDma128<kTileK, W>;
+  constexpr int DK = D / 32;
+  constexpr int DB = D / 16;
+  constexpr int NC = kTileK / 32;  // 32-key chunks (k-steps of the dQ product)
+
+  const int n_q = a.n_q, n_k = a.n_k;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int tile = xcd_remap(wg, a.total_q);
+  const int bh = tile / a.tiles_q;
+  const int qt = tile - bh * a.tiles_q;
+  const int64_t qbase = (int64_t)bh * n_q * D;
+  const int64_t kbase = (int64_t)bh * n_k * D;
+  const int row = qt * (16 * W) + wave * 16 + l16;  // this lane's query
+  const int qrow = min(row, n_q - 1);
+
+  bf16x8 qf[DK], of[DK];  // B operands of S^T = K Q^T and dP^T = V dO^T
+#pragma unroll
+  for (int dk = 0; dk < DK; ++dk) {
+    qf[dk] = *reinterpret_cast<const bf16x8*>(a.Q + qbase + (int64_t)qrow * D + dk * 32 + 8 * g);
+    of[dk] = *reinterpret_cast<const bf16x8*>(a.dO + qbase + (int64_t)qrow * D + dk * 32 + 8 * g);
+  }
+  const float lse = a.Lse2[(int64_t)bh * n_q + qrow];
+  const float nd = a.Dv[(int64_t)bh * n_q + qrow];
+  const f32x4 ndv = f32x4{nd, nd, nd, nd};  // -D: the first dP^T product's accumulator
+
+  f32x4 acc[DB];  // dQ^T: register r of block db -> column 16*db + 4*g + r
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x4{};
+
+  TK dma;
+  dma.init(wave, lane);
+  int a_off[DK], t_off[DB];
+#pragma unroll
+  for (int dk = 0; dk < DK; ++dk) a_off[dk] = L::off(l16, dk * 32 + 8 * g);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) t_off[db] = L::off(4 * g + (l16 >> 2), db * 16 + 4 * (l16 & 3));
+
+  auto tile_body = [&](const bf16* ks, const bf16* vs, int j0, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      bf16x8 sf;  // dS^T of keys 32c + {4g .. 4g+3, 16+4g .. 16+4g+3}
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kb = 2 * c + h;
+        f32x4 s = f32x4{}, dp = ndv;
+#pragma unroll
+        for (int dk = 0; dk < DK; ++dk) {
+          const int off = a_off[dk] + kb * 16 * D;
+          s = mfma16x16x32(lds_read_b128(ks + off), qf[dk], s);
+          dp = mfma16x16x32(lds_read_b128(vs + off), of[dk], dp);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float p = fast_exp2(__builtin_fmaf(s[r], a.C, -lse));
+          if constexpr (kMasked) {
+            if (j0 + kb * 16 + 4 * g + r >= n_k) p = 0.f;  // padding keys
+          }
+          sf[4 * h + r] = (bf16)(p * dp[r]);
+        }
+      }
+      // dQ^T += K^T dS^T over the 32 keys of chunk c
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int o0 = t_off[db] + c * 32 * D, o1 = o0 + 16 * D;
+        const bf16x8 ak = cat(lds_read_tr16(ks + o0), lds_read_tr16(ks + o1));
+        acc[db] = mfma16x16x32(ak, sf, acc[db]);
+      }
+    }
+  };
+
+  const int ntiles = (n_k + kTileK - 1) / kTileK;
+  auto step = [&](const bf16* ks, const bf16* vs, bf16* kn, bf16* vn, int t) {
+    const int j0 = t * kTileK;
+    if (t + 1 < ntiles) {
+      dma.issue(a.K + kbase, j0 + kTileK, n_k, kn);
+      dma.issue(a.V + kbase, j0 + kTileK, n_k, vn);
+    }
+    if (j0 + kTileK <= n_k) tile_body(ks, vs, j0, std::false_type{});
+    else tile_body(ks, vs, j0, std::true_type{});
+    wait_all();
+    __syncthreads();
+  };
+  dma.issue(a.K + kbase, 0, n_k, s0);
+  dma.issue(a.V + kbase, 0, n_k, s1);
+  wait_all();
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    step(s0, s1, s2, s3, t);
+    if (t + 1 < ntiles) step(s2, s3, s0, s1, t + 1);
+  }
+
+  if (row < n_q) {
+    bf16* qout = a.dQ + qbase + (int64_t)row * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      bf16x4 w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = (bf16)(acc[db][r] * a.scale);
+      *reinterpret_cast<bf16x4*>(qout + db * 16 + 4 * g) = w;
+    }
+  }
+}
+
+template <int W>
+__global__ __launch_bounds__(64 * W, 2) void bwd_main128_kernel(BwdArgs a) {
+  constexpr int kElems = SwzDma128<kTileQ, W>::kElems;
+  static_assert(SwzDma128<kTileK, W>::kElems == kElems, "both roles share the LDS arrays");
+  __shared__ __attribute__((aligned(1024))) bf16 s0[kElems];
+  __shared__ __attribute__((aligned(1024))) bf16 s1[kElems];
+  __shared__ __attribute__((aligned(1024))) bf16 s2[kElems];
+  __shared__ __attribute__((aligned(1024))) bf16 s3[kElems];
+  __shared__ __attribute__((aligned(256))) float f0[2 * kTileQ];
+  __shared__ __attribute__((aligned(256))) float f1[2 * kTileQ];
+  const int wg = blockIdx.x;
+  if (wg < a.total_kv) dkdv_role128<W>(a, wg, s0, s1, s2, s3, f0, f1);
+  else dq_role128<W>(a, wg - a.total_kv, s0, s1, s2, s3);
 }
 
 template <int D, int W>
@@ -421,15 +739,52 @@ hipError_t launch(const BwdProblem& p, hipStream_t stream) {
 
 }  // namespace
 
+template <int W>
+hipError_t launch128(const BwdProblem& p, hipStream_t stream) {
+  constexpr int D = 128;
+  const int64_t rows = p.heads * p.rows_q;
+  float* Dv = p.ws;
+  float* Lse2 = p.ws + rows;
+  if (rows > 0) {
+    const int64_t threads = rows * (D / 8);
+    const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL((bwd_rows_kernel<D>), dim3(blocks), dim3(kThreads), 0, stream,
+                       (const bf16*)p.o, (const bf16*)p.dO, p.m, p.l, Dv, Lse2, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  BwdArgs a;
+  a.Q = (const bf16*)p.q;
+  a.K = (const bf16*)p.k;
+  a.V = (const bf16*)p.v;
+  a.dO = (const bf16*)p.dO;
+  a.Dv = Dv;
+  a.Lse2 = Lse2;
+  a.dQ = (bf16*)p.dq;
+  a.dK = (bf16*)p.dk;
+  a.dV = (bf16*)p.dv;
+  a.n_q = p.rows_q;
+  a.n_k = p.n_k;
+  a.tiles_kv = (p.n_k + 16 * W - 1) / (16 * W);
+  a.tiles_q = (p.rows_q + 16 * W - 1) / (16 * W);
+  a.total_kv = (int)(p.heads * a.tiles_kv);
+  a.total_q = (int)(p.heads * a.tiles_q);
+  a.scale = 1.0f / sqrtf((float)D);
+  a.C = kLog2e * a.scale;
+  hipLaunchKernelGGL((bwd_main128_kernel<W>), dim3((unsigned)(a.total_kv + a.total_q)),
+                     dim3(64 * W), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_bf16(int d, const BwdProblem& p, hipStream_t stream) {
-  if (d == 128) return launch<128, kWaves>(p, stream);
   // 8-wave workgroups serve each staged tile to twice the rows (measured 3-4%
   // faster at d = 64) but halve the workgroup count: only on grids that still
   // give every CU one
-  constexpr int64_t rows = 32 * kWideWaves;
+  const int64_t rows = (d == 64 ? 32 : 16) * kWideWaves;
   const int64_t wide_grid = p.heads * ((p.n_k + rows - 1) / rows + (p.rows_q + rows - 1) / rows);
-  if (wide_grid >= kComputeUnits) return launch<64, kWideWaves>(p, stream);
-  return launch<64, kWaves>(p, stream);
+  const bool wide = wide_grid >= kComputeUnits;
+  if (d == 128) return wide ? launch128<kWideWaves>(p, stream) : launch128<kWaves>(p, stream);
+  return wide ? launch<64, kWideWaves>(p, stream) : launch<64, kWaves>(p, stream);
 }
 
 }  // namespace mea

@@ -47,7 +47,7 @@ __device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
 }
 
 // ---------------------------------------------------------------- LDS tiles
-// Padded row-major bf16 tile (used by the backward): each row of D elements is
+// Padded row-major bf16 tile (used by the d = 64 backward): each row of D elements is
 // followed by 16 bytes of padding, so row r starts at byte r*(2D + 16). For
 // D = 64 (144-byte rows) consecutive rows start 36 banks apart: 16 rows read
 // at the same 16-byte column cover all 64 banks once. A transposed read
@@ -62,7 +62,8 @@ struct Padded {
   __device__ static constexpr int off(int row, int col) { return row * kRowElems + col; }
 };
 
-// Swizzled row-major bf16 tile (used by the forward): rows of D elements with no
+// Swizzled row-major bf16 tile (used by the forward and by the d = 128
+// backward): rows of D elements with no
 // padding; the 16-byte chunk c of row r sits at chunk position c ^ swz(r).
 // With 64 banks of 4 bytes, a 16-byte read of one chunk column by 16 lanes
 // (rows r..r+15) touches every bank once, and so does a transposed read by 32

@@ -262,3 +262,30 @@ def test_wide_workgroups_backward_full(B, H, H_kv, n_q, n_k):
     check("dQ", f64(dq.cpu()), rq, "bf16")
     check("dK", f64(dk.cpu()), rk, "bf16")
     check("dV", f64(dv.cpu()), rv, "bf16")
+
+
+@pytest.mark.parametrize("B,H,H_kv,n", [(1, 32, 8, 4096), (1, 4, 4, 3001)])
+def test_backward_d128_long_sampled(B, H, H_kv, n):
+    # the d = 128 backward at a prefill-sized grouped shape (8-wave layout) and a ragged
+    # length (4-wave layout): sampled dQ rows of two query heads and sampled dK, dV rows
+    # of their key/value heads against the oracle
+    say("bwd d128 long", B, H, H_kv, n)
+    t = draw(B, H, H_kv, n, n, 128, "bf16", seed=171 + n, with_do=True)
+    q, k, v, do = (gpu(t[x]) for x in ("q", "k", "v", "do"))
+    o, m, l = mea.attn_fwd_ex(q, k, v)
+    dq, dk, dv = mea.attn_bwd_ex(q, k, v, o, do, m, l)
+    torch.cuda.synchronize()
+    dq, dk, dv = (f64(x.cpu()) for x in (dq, dk, dv))
+    rng = np.random.default_rng(n)
+    rows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 30, replace=False)]))
+    G = H // H_kv
+    for hk in (0, H_kv - 1):
+        qh = slice(hk * G, hk * G + G)  # the query heads of key/value head hk
+        qs, dos = f64(t["q"])[:, qh], f64(t["do"])[:, qh]
+        ks, vs = f64(t["k"])[:, hk:hk + 1], f64(t["v"])[:, hk:hk + 1]
+        rq, rk, rv = oracle.gqa_bwd(qs[:, :1], ks, vs, dos[:, :1], rows=rows,
+                                    cols=np.array([], dtype=np.int64))
+        check("dQ", dq[:, hk * G:hk * G + 1][:, :, rows], rq, "bf16")
+        _, rk, rv = oracle.gqa_bwd(qs, ks, vs, dos, rows=np.array([], dtype=np.int64), cols=rows)
+        check("dK", dk[:, hk:hk + 1][:, :, rows], rk, "bf16")
+        check("dV", dv[:, hk:hk + 1][:, :, rows], rv, "bf16")
