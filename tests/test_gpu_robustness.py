@@ -17,12 +17,13 @@ from test_gpu_parity import check, check_stats, f64, gpu, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("dtype,n", [("bf16", 1 << 20), ("fp32", 1 << 18)])
-def test_forward_longest_sequence_sampled_rows(dtype, n):
-    # one head of 2^20 keys (bf16; 2^18 for the fp64-score fp32 path): row indices,
-    # tile offsets and grids far beyond every workload
-    say("fwd long", dtype, n)
-    t = inputgen.draw(1, 1, n, 64, dtype, seed=101)
+@pytest.mark.parametrize("dtype,d,n", [("bf16", 64, 1 << 20), ("bf16", 128, 1 << 19),
+                                       ("fp32", 64, 1 << 18)])
+def test_forward_longest_sequence_sampled_rows(dtype, d, n):
+    # one head of 2^20 keys (bf16; 2^19 at d = 128; 2^18 for the fp64-score fp32 path):
+    # row indices, tile offsets and grids far beyond every workload
+    say("fwd long", dtype, d, n)
+    t = inputgen.draw(1, 1, n, d, dtype, seed=101)
     o, m, l = mea.attn_fwd(gpu(t["q"]), gpu(t["k"]), gpu(t["v"]))
     torch.cuda.synchronize()
     rows = np.concatenate([np.random.default_rng(102).choice(n, 14, replace=False), [0, n - 1]])
@@ -31,13 +32,13 @@ def test_forward_longest_sequence_sampled_rows(dtype, n):
     check_stats(m.cpu().numpy()[:, :, rows], l.cpu().numpy()[:, :, rows], m_ref, l_ref, dtype)
 
 
-def test_backward_long_sequence_rows_and_identities():
-    # 2^19 tokens: sampled dQ rows against the oracle; dK and dV through identities of
-    # the softmax Jacobian that hold at any length: sum_j dK_j = 0 (each softmax row is
-    # shift-invariant) and sum_j dV_j = sum_i dO_i (each row of P sums to 1)
-    n = 1 << 19
-    say("bwd long", n)
-    t = inputgen.draw(1, 1, n, 64, "bf16", seed=103, with_do=True)
+@pytest.mark.parametrize("d,n", [(64, 1 << 19), (128, 1 << 18)])
+def test_backward_long_sequence_rows_and_identities(d, n):
+    # 2^19 tokens (2^18 at d = 128): sampled dQ rows against the oracle; dK and dV through
+    # identities of the softmax Jacobian that hold at any length: sum_j dK_j = 0 (each
+    # softmax row is shift-invariant) and sum_j dV_j = sum_i dO_i (each row of P sums to 1)
+    say("bwd long", d, n)
+    t = inputgen.draw(1, 1, n, d, "bf16", seed=103, with_do=True)
     q, k, v, do = (gpu(t[x]) for x in ("q", "k", "v", "do"))
     o, m, l = mea.attn_fwd(q, k, v)
     dq, dk, dv = mea.attn_bwd(q, k, v, o, do, m, l)
