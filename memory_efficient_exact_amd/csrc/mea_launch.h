@@ -41,12 +41,13 @@ struct FwdGeometry {
   int key_tile;    // keys per LDS tile (split lengths are multiples of it)
   int resident;    // workgroups that fit on one compute unit at once
 };
-// (both forwards pick a decoding layout for heads with few query rows; the
-// bf16 forward also picks wider workgroups on grids that fill the chip)
+// (both forwards pick a decoding layout for heads with few query rows and for
+// grids too small to occupy half of the chip; the bf16 forward also picks
+// wider workgroups on grids that fill the chip)
 FwdGeometry fwd_geometry_bf16(int d, int64_t heads, int64_t rows_q);
-FwdGeometry fwd_geometry_f32(int d, int64_t rows_q);
+FwdGeometry fwd_geometry_f32(int d, int64_t heads, int64_t rows_q);
 inline FwdGeometry fwd_geometry(bool bf16, int d, int64_t heads, int64_t rows_q) {
-  return bf16 ? fwd_geometry_bf16(d, heads, rows_q) : fwd_geometry_f32(d, rows_q);
+  return bf16 ? fwd_geometry_bf16(d, heads, rows_q) : fwd_geometry_f32(d, heads, rows_q);
 }
 
 // Forward pass (final or, with p.splits > 1, partial) for bf16 / fp32 inputs.

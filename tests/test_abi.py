@@ -278,15 +278,25 @@ def test_split_planning(L, dt, d, tile):
 
 
 def test_split_planning_full_tiles(L):
-    # more than 64 query rows per head: the regular layouts (bf16 d = 128 uses 64-key tiles)
+    # more than 64 (bf16) or 32 (fp32) query rows per head on grids of more than 128
+    # row-tiled 4-wave workgroups: the regular layouts (bf16 d = 128 uses 64-key tiles,
+    # fp32 32-key tiles)
     ns = mea.attn_fwd_splitkv_num_splits
-    assert ns(BF16, 1, 1, 1, 4096, 4096, 128, 10 ** 6) == 4096 // 64
-    assert ns(BF16, 1, 1, 1, 4096, 4096, 64, 10 ** 6) == 4096 // 128
-    assert ns(BF16, 1, 1, 1, 65, 4096, 128, 10 ** 6) == 4096 // 64
-    assert ns(BF16, 1, 1, 1, 64, 4096, 128, 10 ** 6) == 4096 // 128   # still decoding
-    assert ns(F32, 1, 1, 1, 4096, 4096, 128, 10 ** 6) == 4096 // 32
-    assert ns(F32, 1, 1, 1, 33, 4096, 64, 10 ** 6) == 4096 // 32
-    assert ns(F32, 1, 1, 1, 32, 4096, 64, 10 ** 6) == 4096 // 64     # fp32 decoding
+    big = 10 ** 6
+    assert ns(BF16, 1, 64, 64, 4096, 4096, 128, big) == 4096 // 64
+    assert ns(BF16, 1, 64, 64, 4096, 4096, 64, big) == 4096 // 128
+    assert ns(BF16, 1, 256, 256, 65, 4096, 128, big) == 4096 // 64
+    assert ns(BF16, 1, 256, 256, 64, 4096, 128, big) == 4096 // 128  # still decoding
+    assert ns(F32, 1, 64, 64, 4096, 4096, 128, big) == 4096 // 32
+    assert ns(F32, 1, 256, 256, 33, 4096, 64, big) == 4096 // 32
+    assert ns(F32, 1, 256, 256, 32, 4096, 64, big) == 4096 // 64     # fp32 decoding
+    # grids of at most 128 row-tiled workgroups take the decoding layouts at any row count
+    assert ns(BF16, 1, 1, 1, 4096, 4096, 128, big) == 4096 // 128
+    assert ns(BF16, 1, 64, 64, 256, 4096, 128, big) == 4096 // 128   # 128 workgroups
+    assert ns(BF16, 1, 65, 65, 256, 4096, 128, big) == 4096 // 64    # 130
+    assert ns(F32, 1, 1, 1, 4096, 4096, 64, big) == 4096 // 64
+    assert ns(F32, 1, 64, 64, 128, 4096, 64, big) == 4096 // 64      # 128 workgroups
+    assert ns(F32, 1, 65, 65, 128, 4096, 64, big) == 4096 // 32      # 130
 
 
 def test_split_validation(L):

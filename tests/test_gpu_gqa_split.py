@@ -242,6 +242,37 @@ def test_wide_workgroups_full(B, H, H_kv, n_q, n_k, d, splits):
     check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, "bf16")
 
 
+# Row-tiled 4-wave forward workgroups. Grids of at most 128 such workgroups
+# take the decoding layout instead (keys split across the waves), so these
+# shapes sit between 128 and 256 workgroups: bf16 at d = 64 (256 rows per
+# workgroup) and d = 128 (128 rows), fp32 (64 rows), with ragged tiles and
+# grouped heads.
+ROW_TILED_CASES = [("bf16", 1, 33, 33, 1000, 300, 64), ("bf16", 2, 64, 16, 300, 257, 64),
+                   ("bf16", 1, 17, 17, 1000, 333, 128), ("fp32", 1, 9, 9, 1000, 300, 64),
+                   ("fp32", 1, 12, 3, 1000, 200, 128)]
+
+
+@pytest.mark.parametrize("dtype,B,H,H_kv,n_q,n_k,d", ROW_TILED_CASES)
+@pytest.mark.parametrize("splits", [None, 3])
+def test_row_tiled_workgroups_full(dtype, B, H, H_kv, n_q, n_k, d, splits):
+    rows = {("bf16", 64): 256, ("bf16", 128): 128}.get((dtype, d), 64)
+    grid = B * H_kv * -(-(H // H_kv) * n_q // rows)
+    assert 128 < grid < 256  # the row-tiled 4-wave layout is taken
+    say("row-tiled", dtype, B, H, H_kv, n_q, n_k, d, splits)
+    t = draw(B, H, H_kv, n_q, n_k, d, dtype, seed=171 + n_q + d)
+    q, k, v = (gpu(t[x]) for x in ("q", "k", "v"))
+    if splits is None:
+        o, m, l = mea.attn_fwd_ex(q, k, v)
+    else:
+        dt = mea.DTYPE_BF16 if dtype == "bf16" else mea.DTYPE_F32
+        assert mea.attn_fwd_splitkv_num_splits(dt, B, H, H_kv, n_q, n_k, d, splits) > 1
+        o, m, l = mea.attn_fwd_splitkv(q, k, v, num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, m_ref, l_ref = oracle.gqa_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]))
+    check("O", f64(o.cpu()), o_ref, dtype)
+    check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, dtype)
+
+
 # The bf16 backward at d = 64 takes 8-wave workgroups (256 keys or queries each)
 # when heads x (key tiles + query tiles) of that size reach 256: ragged tiles on both
 # sides, grouped heads, and fewer keys than one workgroup covers.
