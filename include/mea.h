@@ -37,7 +37,10 @@
  *    hipGetLastError right after the launch; faults during execution surface
  *    at the caller's next synchronisation, as with any HIP kernel.
  *  - Supported: dt in {MEA_DTYPE_BF16, MEA_DTYPE_F32}, d in {64, 128},
- *    n (and n_q, n_k, and (H/H_kv)*n_q) <= 2^24, B*H <= 2^24.
+ *    n (and n_q, n_k, and (H/H_kv)*n_q) <= 2^24, B*H <= 2^24, and
+ *    B*H_kv * ceil(max((H/H_kv)*n_q, n_k) / 64) <= 2^22 (B*H * ceil(n / 64)
+ *    for the self-attention calls), which keeps every launch grid within 2^31
+ *    work-items. Larger shapes are rejected with MEA_ERR_SHAPE.
  *  - Accuracy: bf16 inputs are multiplied exactly on bf16 MFMA with fp32
  *    accumulation; probabilities are rounded to bf16 (round-to-nearest-even)
  *    for the P V product; outputs are rounded to bf16 (RNE). fp32 inputs

@@ -63,21 +63,24 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(
     const float* __restrict__ Ls, float* __restrict__ Dv, float* __restrict__ Lse2,
     int64_t rows) {
   constexpr int LPR = D / 8;  // lanes per row
-  const int64_t gtid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t row = gtid / LPR;
-  const int part = (int)(gtid - row * LPR);
-  float acc = 0.f;
-  if (row < rows) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(O + row * D + part * 8);
-    const bf16x8 b = *reinterpret_cast<const bf16x8*>(dO + row * D + part * 8);
+  constexpr int RPB = kThreads / LPR;  // rows per workgroup and pass
+  const int part = threadIdx.x % LPR;
+  // workgroup-uniform stride over the rows (the grid may be capped)
+  for (int64_t r0 = (int64_t)blockIdx.x * RPB; r0 < rows; r0 += (int64_t)gridDim.x * RPB) {
+    const int64_t row = r0 + threadIdx.x / LPR;
+    float acc = 0.f;
+    if (row < rows) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(O + row * D + part * 8);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(dO + row * D + part * 8);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b[e], acc);
-  }
+      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b[e], acc);
+    }
 #pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && part == 0) {
-    Dv[row] = -acc;  // stored negated: it seeds the dP accumulators below
-    Lse2[row] = Mx[row] * kLog2e + __builtin_log2f(Ls[row]);
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (row < rows && part == 0) {
+      Dv[row] = -acc;  // stored negated: it seeds the dP accumulators below
+      Lse2[row] = Mx[row] * kLog2e + __builtin_log2f(Ls[row]);
+    }
   }
 }
 
@@ -720,8 +723,7 @@ hipError_t launch(const BwdProblem& p, hipStream_t stream) {
   float* Dv = p.ws;
   float* Lse2 = p.ws + rows;
   if (rows > 0) {
-    const int64_t threads = rows * (D / 8);
-    const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
+    const unsigned blocks = row_blocks(rows, kThreads / (D / 8));
     hipLaunchKernelGGL((bwd_rows_kernel<D>), dim3(blocks), dim3(kThreads), 0, stream,
                        (const bf16*)p.o, (const bf16*)p.dO, p.m, p.l, Dv, Lse2, rows);
     hipError_t e = hipGetLastError();
@@ -759,8 +761,7 @@ hipError_t launch128(const BwdProblem& p, hipStream_t stream) {
   float* Dv = p.ws;
   float* Lse2 = p.ws + rows;
   if (rows > 0) {
-    const int64_t threads = rows * (D / 8);
-    const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
+    const unsigned blocks = row_blocks(rows, kThreads / (D / 8));
     hipLaunchKernelGGL((bwd_rows_kernel<D>), dim3(blocks), dim3(kThreads), 0, stream,
                        (const bf16*)p.o, (const bf16*)p.dO, p.m, p.l, Dv, Lse2, rows);
     hipError_t e = hipGetLastError();

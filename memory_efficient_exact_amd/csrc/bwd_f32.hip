@@ -64,23 +64,26 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_f32_kernel(
     const float* __restrict__ O, const float* __restrict__ dO, const float* __restrict__ Mx,
     const float* __restrict__ Ls, RowTerm* __restrict__ terms, int64_t rows) {
   constexpr int LPR = D / 4;
-  const int64_t gtid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t row = gtid / LPR;
-  const int part = (int)(gtid - row * LPR);
-  double acc = 0.0;
-  if (row < rows) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(O + row * D + part * 4);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(dO + row * D + part * 4);
+  constexpr int RPB = kThreads / LPR;  // rows per workgroup and pass
+  const int part = threadIdx.x % LPR;
+  // workgroup-uniform stride over the rows (the grid may be capped)
+  for (int64_t r0 = (int64_t)blockIdx.x * RPB; r0 < rows; r0 += (int64_t)gridDim.x * RPB) {
+    const int64_t row = r0 + threadIdx.x / LPR;
+    double acc = 0.0;
+    if (row < rows) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(O + row * D + part * 4);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(dO + row * D + part * 4);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc = __builtin_fma((double)a[e], (double)b[e], acc);
-  }
+      for (int e = 0; e < 4; ++e) acc = __builtin_fma((double)a[e], (double)b[e], acc);
+    }
 #pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && part == 0) {
-    RowTerm t;
-    t.lse2 = (double)Mx[row] * 1.4426950408889634 + log2((double)Ls[row]);
-    t.neg_d = -acc;
-    terms[row] = t;
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (row < rows && part == 0) {
+      RowTerm t;
+      t.lse2 = (double)Mx[row] * 1.4426950408889634 + log2((double)Ls[row]);
+      t.neg_d = -acc;
+      terms[row] = t;
+    }
   }
 }
 
@@ -348,8 +351,7 @@ hipError_t launch(const BwdProblem& p, hipStream_t stream) {
   const int64_t rows = p.heads * p.rows_q;
   RowTerm* terms = reinterpret_cast<RowTerm*>(p.ws);
   if (rows > 0) {
-    const int64_t threads = rows * (D / 4);
-    const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
+    const unsigned blocks = row_blocks(rows, kThreads / (D / 4));
     hipLaunchKernelGGL((bwd_rows_f32_kernel<D>), dim3(blocks), dim3(kThreads), 0, stream,
                        (const float*)p.o, (const float*)p.dO, p.m, p.l, terms, rows);
     hipError_t e = hipGetLastError();

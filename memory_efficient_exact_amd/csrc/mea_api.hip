@@ -12,11 +12,16 @@
 namespace {
 
 constexpr int kVersion = 300;  // 0.3.0
-// The largest grids are (heads * ceil(rows/64)) workgroups of 256 threads;
-// keep them (and all row indices) comfortably inside 32 bits.
+// Grid bounds. With heads * ceil(max(rows_q, n_k) / 64) <= kMaxBlocks, the
+// tiled grids stay within 2^31 work-items: the largest give every 64 rows at
+// most two workgroups of 256 threads (the backward's dK/dV plus dQ workgroups
+// at 64 rows each, the decoding forwards' 32- or 16-row workgroups for heads
+// of at most 64 or 32 rows), and a split grid is checked against the same
+// bound. The per-row kernels (row terms, merge) cap their grids and stride.
+// Row indices within a head stay below 2^24.
 constexpr int64_t kMaxN = int64_t(1) << 24;
 constexpr int64_t kMaxBH = int64_t(1) << 24;
-constexpr int64_t kMaxBlocks = int64_t(1) << 23;
+constexpr int64_t kMaxBlocks = int64_t(1) << 22;
 // Split-key planning: at most this many key ranges per head; the automatic
 // choice splits only grids smaller than one full round of resident
 // workgroups (compute units x the forward kernel's workgroups per CU) and

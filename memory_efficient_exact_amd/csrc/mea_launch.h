@@ -56,6 +56,17 @@ hipError_t launch_fwd_f32(int d, const FwdProblem& p, hipStream_t stream);
 // Merge of the split partials in p.part into p.o, p.m, p.l.
 hipError_t launch_merge(bool bf16, int d, const FwdProblem& p, hipStream_t stream);
 
+// Grid of the per-row kernels (backward row terms, split merge): one pass of
+// rows_per_block rows per workgroup, capped at kRowBlocks workgroups (2^21
+// threads of 256, enough to keep HBM busy); the kernels stride over the
+// remaining rows, so every grid stays far below the 2^32 work-item limit of
+// a dispatch whatever the row count.
+constexpr int64_t kRowBlocks = int64_t(1) << 13;
+inline unsigned row_blocks(int64_t rows, int64_t rows_per_block) {
+  const int64_t b = (rows + rows_per_block - 1) / rows_per_block;
+  return (unsigned)(b < kRowBlocks ? b : kRowBlocks);
+}
+
 struct BwdProblem {
   int64_t heads = 0;  // B * H_kv
   int rows_q = 0;     // G * n_q

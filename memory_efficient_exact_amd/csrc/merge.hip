@@ -61,85 +61,92 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeArgs a) {
   const int rl = t / TPR;
   const int j = (t - rl * TPR) / CL;
   const int c = t - rl * TPR - j * CL;
-  const int64_t row = (int64_t)blockIdx.x * RPW + rl;
-  const bool live = row < a.rows;  // every thread reaches both barriers
-
-  const float* rec0 = a.Ps + row * 4;
   const int64_t rstride = a.rows * 4;
-  const float* po0 = a.Po + row * D + c * 4;
   const int64_t pstride = a.rows * D;
 
-  // 1. largest reference (and, for bf16, largest raw score) over this lane's ranges
-  double ref = -INFINITY;
-  float raw = -INFINITY;
-  if (live) {
-    for (int s = j; s < a.splits; s += SL) {
-      const float* r = rec0 + s * rstride;
-      if constexpr (kBf16) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(r);
-        raw = fmaxf(raw, v[0]);
-        ref = fmax(ref, (double)v[1]);
-      } else {
-        ref = fmax(ref, *reinterpret_cast<const double*>(r));
-      }
-    }
-  }
-  if (c == 0) {
-    s_ref[rl][j] = ref;
-    s_raw[rl][j] = raw;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < SL; ++i) {
-    ref = fmax(ref, s_ref[rl][i]);
-    raw = fmaxf(raw, s_raw[rl][i]);
-  }
+  // workgroup-uniform stride over the rows (the grid may be capped). The two
+  // barriers of a pass also order it against the next: a pass writes s_ref
+  // only after every thread has read the previous pass's values (before its
+  // second barrier), and s_acc only after every thread has finished the
+  // previous pass (its first barrier).
+  for (int64_t r0 = (int64_t)blockIdx.x * RPW; r0 < a.rows; r0 += (int64_t)gridDim.x * RPW) {
+    const int64_t row = r0 + rl;
+    const bool live = row < a.rows;  // every thread reaches both barriers
+    const float* rec0 = a.Ps + row * 4;
+    const float* po0 = a.Po + row * D + c * 4;
 
-  // 2. this lane's ranges, re-based on the common reference
-  f32x4 acc = f32x4{};
-  float L = 0.f;
-  if (live) {
-    const float refb = (float)ref;  // bf16: an fp32 value already
-    for (int s = j; s < a.splits; s += SL) {
-      const float* r = rec0 + s * rstride;
-      float w;
-      if constexpr (kBf16) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(r);
-        w = v[2] * fast_exp2(v[1] - refb);
-      } else {
-        w = r[2] * fast_exp2((float)((*reinterpret_cast<const double*>(r) - ref) * a.C64));
+    // 1. largest reference (and, for bf16, largest raw score) over this lane's ranges
+    double ref = -INFINITY;
+    float raw = -INFINITY;
+    if (live) {
+      for (int s = j; s < a.splits; s += SL) {
+        const float* r = rec0 + s * rstride;
+        if constexpr (kBf16) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(r);
+          raw = fmaxf(raw, v[0]);
+          ref = fmax(ref, (double)v[1]);
+        } else {
+          ref = fmax(ref, *reinterpret_cast<const double*>(r));
+        }
       }
-      L += w;
-      acc += w * *reinterpret_cast<const f32x4*>(po0 + s * pstride);
     }
-  }
-  s_acc[rl][j][c] = acc;
-  if (c == 0) s_sum[rl][j] = L;
-  __syncthreads();
-  if (!live || j != 0) return;
-#pragma unroll
-  for (int i = 1; i < SL; ++i) {
-    acc += s_acc[rl][i][c];
-    L += s_sum[rl][i];
-  }
-  const float inv = 1.f / L;
-  if constexpr (kBf16) {
-    bf16x4 o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = (bf16)(acc[e] * inv);
-    *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.O) + row * D + c * 4) = o;
-    if (a.Mx != nullptr && c == 0) {
-      a.Mx[row] = raw * a.scale;
-      a.Ls[row] = L * fast_exp2(-__builtin_fmaf(raw, a.C, -(float)ref));
+    if (c == 0) {
+      s_ref[rl][j] = ref;
+      s_raw[rl][j] = raw;
     }
-  } else {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(a.O) + row * D + c * 4) = acc * inv;
-    if (a.Mx != nullptr && c == 0) {
-      // as in the unsplit kernel: l against the reported (rounded) maximum
-      const double m_nat = ref * a.scale64;
-      const float m_st = (float)m_nat;
-      a.Mx[row] = m_st;
-      a.Ls[row] = (float)((double)L * exp(m_nat - (double)m_st));
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < SL; ++i) {
+      ref = fmax(ref, s_ref[rl][i]);
+      raw = fmaxf(raw, s_raw[rl][i]);
+    }
+
+    // 2. this lane's ranges, re-based on the common reference
+    f32x4 acc = f32x4{};
+    float L = 0.f;
+    if (live) {
+      const float refb = (float)ref;  // bf16: an fp32 value already
+      for (int s = j; s < a.splits; s += SL) {
+        const float* r = rec0 + s * rstride;
+        float w;
+        if constexpr (kBf16) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(r);
+          w = v[2] * fast_exp2(v[1] - refb);
+        } else {
+          w = r[2] * fast_exp2((float)((*reinterpret_cast<const double*>(r) - ref) * a.C64));
+        }
+        L += w;
+        acc += w * *reinterpret_cast<const f32x4*>(po0 + s * pstride);
+      }
+    }
+    s_acc[rl][j][c] = acc;
+    if (c == 0) s_sum[rl][j] = L;
+    __syncthreads();
+    if (!live || j != 0) continue;
+#pragma unroll
+    for (int i = 1; i < SL; ++i) {
+      acc += s_acc[rl][i][c];
+      L += s_sum[rl][i];
+    }
+    const float inv = 1.f / L;
+    if constexpr (kBf16) {
+      bf16x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (bf16)(acc[e] * inv);
+      *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.O) + row * D + c * 4) = o;
+      if (a.Mx != nullptr && c == 0) {
+        a.Mx[row] = raw * a.scale;
+        a.Ls[row] = L * fast_exp2(-__builtin_fmaf(raw, a.C, -(float)ref));
+      }
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(a.O) + row * D + c * 4) = acc * inv;
+      if (a.Mx != nullptr && c == 0) {
+        // as in the unsplit kernel: l against the reported (rounded) maximum
+        const double m_nat = ref * a.scale64;
+        const float m_st = (float)m_nat;
+        a.Mx[row] = m_st;
+        a.Ls[row] = (float)((double)L * exp(m_nat - (double)m_st));
+      }
     }
   }
 }
@@ -147,8 +154,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeArgs a) {
 template <int D, bool kBf16, int SL>
 hipError_t launch_sl(const MergeArgs& a, hipStream_t stream) {
   constexpr int RPW = kThreads / (D / 4 * SL);
-  const int64_t blocks = (a.rows + RPW - 1) / RPW;
-  hipLaunchKernelGGL((merge_kernel<D, kBf16, SL>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((merge_kernel<D, kBf16, SL>), dim3(row_blocks(a.rows, RPW)), dim3(kThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

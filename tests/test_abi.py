@@ -85,6 +85,9 @@ def test_fwd_validation(L):
     assert fwd(L, n=-1) == SHAPE
     assert fwd(L, n=(1 << 24) + 1) == SHAPE
     assert fwd(L, B=1 << 20, H=1 << 20) == SHAPE
+    # grid bound: B*H * ceil(n / 64) <= 2^22 keeps every launch within 2^31 work-items
+    assert fwd(L, B=1, H=(1 << 22) + 1, n=64) == SHAPE
+    assert fwd(L, B=1 << 10, H=1 << 10, n=(1 << 12) + 1) == SHAPE
     assert fwd(L, d=96) == UNSUP
     assert fwd(L, d=32) == UNSUP
     assert fwd(L, q=0) == NULL
@@ -208,6 +211,9 @@ def test_fwd_ex_validation(L):
     assert fwd_ex(L, n_k=-1) == SHAPE
     assert fwd_ex(L, n_k=(1 << 24) + 1) == SHAPE
     assert fwd_ex(L, H=8, H_kv=1, n_q=(1 << 22)) == SHAPE   # G * n_q rows > 2^24
+    # B*H_kv * ceil(max(G*n_q, n_k) / 64) > 2^22
+    assert fwd_ex(L, B=1 << 19, H=8, H_kv=8, n_q=65, n_k=64) == SHAPE
+    assert fwd_ex(L, B=1 << 19, H=8, H_kv=8, n_q=64, n_k=65) == SHAPE
     assert fwd_ex(L, n_k=0) == SHAPE           # queries but no keys
     assert fwd_ex(L, d=80) == UNSUP
     assert fwd_ex(L, k=0) == NULL

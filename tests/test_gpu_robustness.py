@@ -32,13 +32,17 @@ def test_forward_longest_sequence_sampled_rows(dtype, d, n):
     check_stats(m.cpu().numpy()[:, :, rows], l.cpu().numpy()[:, :, rows], m_ref, l_ref, dtype)
 
 
-@pytest.mark.parametrize("d,n", [(64, 1 << 19), (128, 1 << 18)])
-def test_backward_long_sequence_rows_and_identities(d, n):
-    # 2^19 tokens (2^18 at d = 128): sampled dQ rows against the oracle; dK and dV through
-    # identities of the softmax Jacobian that hold at any length: sum_j dK_j = 0 (each
-    # softmax row is shift-invariant) and sum_j dV_j = sum_i dO_i (each row of P sums to 1)
-    say("bwd long", d, n)
-    t = inputgen.draw(1, 1, n, d, "bf16", seed=103, with_do=True)
+@pytest.mark.parametrize("dtype,d,n", [("bf16", 64, 1 << 19), ("bf16", 128, 1 << 18),
+                                       ("fp32", 64, (1 << 17) + 1000),
+                                       ("fp32", 128, (1 << 16) + 1000)])
+def test_backward_long_sequence_rows_and_identities(dtype, d, n):
+    # 2^19 tokens (2^18 at d = 128; fp32 just over 2^17 and 2^16, so that the row-term
+    # pass strides over its rows more than once): sampled dQ rows against the oracle;
+    # dK and dV through identities of the softmax Jacobian that hold at any length:
+    # sum_j dK_j = 0 (each softmax row is shift-invariant) and sum_j dV_j = sum_i dO_i
+    # (each row of P sums to 1)
+    say("bwd long", dtype, d, n)
+    t = inputgen.draw(1, 1, n, d, dtype, seed=103, with_do=True)
     q, k, v, do = (gpu(t[x]) for x in ("q", "k", "v", "do"))
     o, m, l = mea.attn_fwd(q, k, v)
     dq, dk, dv = mea.attn_bwd(q, k, v, o, do, m, l)
@@ -46,7 +50,7 @@ def test_backward_long_sequence_rows_and_identities(d, n):
     rows = np.concatenate([np.random.default_rng(104).choice(n, 14, replace=False), [0, n - 1]])
     rq, _, _ = oracle.naive_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]), rows=rows,
                                 cols=np.array([], dtype=np.int64), row_block=16)
-    check("dQ", f64(dq.cpu())[:, :, rows], rq, "bf16")
+    check("dQ", f64(dq.cpu())[:, :, rows], rq, dtype)
     dk64, dv64, do64 = f64(dk.cpu())[0, 0], f64(dv.cpu())[0, 0], f64(t["do"])[0, 0]
     assert np.all(np.isfinite(dk64)) and np.all(np.isfinite(dv64))
     scale_k = np.abs(dk64).sum(axis=0)
