@@ -123,6 +123,57 @@ def cpu_baseline(w):
     }
 
 
+def clock_under_load(step, dev, settle_s=1.5, gap_s=1.0):
+    """Graphics clocks of the XCDs, read with `amd-smi metric --clock` while `step`
+    runs back to back on another thread (after the timed steps, so the timed region
+    is undisturbed). The kernels run below the 2.4 GHz the published peak assumes.
+    The tool reports a value that trails the load by up to about a second, so it is
+    read after `settle_s` of load and again `gap_s` later, and the later reading is
+    reported. Returns None when the tool is missing or its output cannot be read."""
+    import shutil
+    import subprocess
+    import threading
+
+    import torch
+    tool = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    done = threading.Event()
+
+    def load():
+        while not done.is_set():
+            step()
+            torch.cuda.synchronize(dev)
+
+    def read():
+        r = subprocess.run([tool, "metric", "--clock", "--json"], capture_output=True, text=True,
+                           timeout=60)
+        data = json.loads(r.stdout)
+        gpus = data.get("gpu_data", data) if isinstance(data, dict) else data
+        clocks = gpus[0]["clock"]
+        return [float(v["clk"]["value"]) for key, v in clocks.items()
+                if key.startswith("gfx_") and isinstance(v, dict) and "clk" in v]
+
+    th = threading.Thread(target=load)
+    th.start()
+    try:
+        time.sleep(settle_s)
+        first = read()
+        time.sleep(gap_s)
+        mhz = read()
+    except (OSError, ValueError, KeyError, IndexError, TypeError, subprocess.SubprocessError):
+        return None
+    finally:
+        done.set()
+        th.join()
+    if not mhz:
+        return None
+    mean = statistics.mean(mhz)
+    return {"gfx_mhz_mean": mean, "gfx_mhz_min": min(mhz), "gfx_mhz_max": max(mhz),
+            "xcds": len(mhz), "earlier_reading_mhz_mean": statistics.mean(first) if first else None,
+            "peak_bf16_tflops_at_clock": PEAK_BF16_TFLOPS * mean / 2400.0,
+            "source": f"amd-smi metric --clock after {settle_s + gap_s:.1f} s of the step run back "
+                      "to back, after the timed steps"}
+
+
 def sweep_configs(steps, warmup):
     """Per workload: forward and backward time, TFLOP/s, peak extra device
     memory beyond inputs and outputs, and the n^2 fp32 score-matrix size."""
@@ -423,6 +474,11 @@ def main():
                    "n2_fp32_score_matrix_bytes": 4 * w.B * w.H * w.n * w.n},
         "roofline": roofline,
     }
+    out["clock"] = clock_under_load(step, dev)
+    if out["clock"] is not None:
+        out["roofline"]["frac_at_clock"] = bwd_tf / out["clock"]["peak_bf16_tflops_at_clock"]
+        log(f"gfx clock under load: {out['clock']['gfx_mhz_mean']:.0f} MHz (mean of "
+            f"{out['clock']['xcds']} XCDs)")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one head ...")
         out["cpu_baseline"] = cpu_baseline(w)
