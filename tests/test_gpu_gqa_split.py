@@ -273,6 +273,27 @@ def test_row_tiled_workgroups_full(dtype, B, H, H_kv, n_q, n_k, d, splits):
     check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, dtype)
 
 
+# Grids of at most 128 row-tiled workgroups take the decoding layout whatever
+# the number of query rows: thousands of rows per head here, grouped heads,
+# ragged key counts, and one shape exactly at the 128-workgroup threshold.
+DECODE_GRID_CASES = [("bf16", 1, 1, 1, 8192, 8192, 64), ("bf16", 1, 2, 1, 4096, 3000, 128),
+                     ("fp32", 1, 2, 2, 2000, 2100, 64), ("fp32", 2, 4, 2, 1000, 777, 128)]
+
+
+@pytest.mark.parametrize("dtype,B,H,H_kv,n_q,n_k,d", DECODE_GRID_CASES)
+def test_small_grid_decoding_layout_full(dtype, B, H, H_kv, n_q, n_k, d):
+    rows = {("bf16", 64): 256, ("bf16", 128): 128}.get((dtype, d), 64)
+    grid = B * H_kv * -(-(H // H_kv) * n_q // rows)
+    assert 2 * grid <= 256 and (H // H_kv) * n_q > 64  # decoding layout by grid size only
+    say("small-grid decode", dtype, B, H, H_kv, n_q, n_k, d)
+    t = draw(B, H, H_kv, n_q, n_k, d, dtype, seed=181 + n_q + d)
+    o, m, l = mea.attn_fwd_ex(gpu(t["q"]), gpu(t["k"]), gpu(t["v"]))
+    torch.cuda.synchronize()
+    o_ref, m_ref, l_ref = oracle.gqa_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]))
+    check("O", f64(o.cpu()), o_ref, dtype)
+    check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, dtype)
+
+
 # The bf16 backward at d = 64 takes 8-wave workgroups (256 keys or queries each)
 # when heads x (key tiles + query tiles) of that size reach 256: ragged tiles on both
 # sides, grouped heads, and fewer keys than one workgroup covers.
