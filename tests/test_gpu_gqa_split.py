@@ -294,6 +294,24 @@ def test_small_grid_decoding_layout_full(dtype, B, H, H_kv, n_q, n_k, d):
     check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, dtype)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_small_grid_decoding_layout_fp32_stress_full(d):
+    # fp32 at the x30 score scale of the stress workload (scores of ~1e4), on a grid
+    # small enough for the decoding layout: the waves' partial results, each formed
+    # against its own fp64 maximum, merge through LDS within the 1e-5 bar
+    B, H, H_kv, n_q, n_k = 1, 2, 2, 2048, 2048
+    grid = B * H_kv * -(-n_q // 64)
+    assert 2 * grid <= 256
+    say("small-grid decode fp32 x30", d)
+    t = draw(B, H, H_kv, n_q, n_k, d, "fp32", seed=191 + d, qk_scale=30.0)
+    o, m, l = mea.attn_fwd_ex(gpu(t["q"]), gpu(t["k"]), gpu(t["v"]))
+    torch.cuda.synchronize()
+    o_ref, m_ref, l_ref = oracle.gqa_fwd(f64(t["q"]), f64(t["k"]), f64(t["v"]))
+    assert np.abs(m_ref).max() > 1e3  # the stress scale is reached
+    check("O", f64(o.cpu()), o_ref, "fp32")
+    check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, "fp32")
+
+
 # The bf16 backward at d = 64 takes 8-wave workgroups (256 keys or queries each)
 # when heads x (key tiles + query tiles) of that size reach 256: ragged tiles on both
 # sides, grouped heads, and fewer keys than one workgroup covers.
