@@ -299,8 +299,10 @@ def sweep_memory():
     """Device memory of a forward and of a forward + backward at n = 1024 .. 16384
     (B=1, H=16, d=64, bf16), outputs allocated by the binding: the peak beyond the
     inputs and outputs (the method's overhead) must be the 8 bytes of row
-    statistics per query row, plus 8 more of backward workspace, at every n,
-    against 4*B*H*n^2 bytes for an fp32 score matrix."""
+    statistics per query row, plus 8 more of backward workspace (the minimum, the
+    row terms), at every n, against 4*B*H*n^2 bytes for an fp32 score matrix. The
+    workspace size the query reports (larger on small grids, where the backward
+    splits its sweeps) is listed beside it."""
     import torch
 
     import inputgen
@@ -319,17 +321,19 @@ def sweep_memory():
         o, m, l = mea.attn_fwd(q, k, v)
         torch.cuda.synchronize(dev)
         fwd_over = torch.cuda.max_memory_allocated(dev) - base - io  # beyond the output O
-        dq, dk, dv = mea.attn_bwd(q, k, v, o, do, m, l)
+        ws = torch.empty(8 * B * H * n, dtype=torch.uint8, device=dev)  # the row terms
+        dq, dk, dv = mea.attn_bwd(q, k, v, o, do, m, l, workspace=ws)
         torch.cuda.synchronize(dev)
         step_over = torch.cuda.max_memory_allocated(dev) - base - 4 * io  # beyond O, dQ, dK, dV
         row = {"n": n, "B": B, "H": H, "d": d, "fwd_overhead_bytes": fwd_over,
                "fwd_overhead_per_row": fwd_over / (B * H * n),
                "step_overhead_bytes": step_over,
                "step_overhead_per_row": step_over / (B * H * n),
+               "bwd_workspace_query_bytes": mea.attn_bwd_workspace_bytes(mea.DTYPE_BF16, B, H, n, d),
                "n2_fp32_score_bytes": 4 * B * H * n * n}
         rows.append(row)
         log(json.dumps(row))
-        del t, q, k, v, do, o, m, l, dq, dk, dv
+        del t, q, k, v, do, o, m, l, dq, dk, dv, ws
         torch.cuda.empty_cache()
     return {"mode": "memory", "rows": rows}
 

@@ -107,10 +107,17 @@ MEA_API mea_status_t attn_fwd(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, i
                       float* row_max, float* row_sum, void* stream);
 
 /*
- * attn_bwd_workspace_bytes - bytes of device workspace attn_bwd needs per
- * query row, times B*H*n: 8 for bf16 (D_i = sum_c dO_ic * O_ic and the base-2
- * log-sum-exp of the row, both fp32), 16 for fp32 (the log-sum-exp in fp64,
- * D_i in fp32, padding). Returns 0 for empty or invalid shapes.
+ * attn_bwd_workspace_bytes - bytes of device workspace attn_bwd is best given.
+ *
+ * The minimum is the row terms: 8 bytes per query row for bf16 (D_i =
+ * sum_c dO_ic * O_ic and the base-2 log-sum-exp of the row, both fp32), 16
+ * for fp32 (the log-sum-exp in fp64, D_i), times B*H*n. On a grid too small to
+ * fill the GPU (at most 256 workgroups of the unsplit backward) the returned
+ * size adds room for a split backward: each workgroup's sweep is cut into up
+ * to 16 ranges, each writing fp32 partial gradients that a reduce pass sums
+ * (at most 32 MiB in all). With only the minimum, attn_bwd runs
+ * unsplit; the results agree to fp32 rounding of the partial sums.
+ * Returns 0 for empty or invalid shapes.
  */
 MEA_API size_t attn_bwd_workspace_bytes(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d);
 
@@ -130,9 +137,13 @@ MEA_API size_t attn_bwd_workspace_bytes(mea_dtype_t dt, int64_t B, int64_t H, in
  * row_max, row_sum : the fp32 [B,H,n] statistics attn_fwd wrote for these
  *                    inputs (required).
  * dq, dk, dv : outputs [B,H,n,d] in dt; fully overwritten.
- * workspace  : device scratch of at least attn_bwd_workspace_bytes(...) bytes,
- *              16-byte aligned, owned by the caller; its contents on entry do
- *              not matter and on return are unspecified.
+ * workspace  : device scratch, 16-byte aligned, owned by the caller: at least
+ *              the row terms (8*B*H*n bytes for bf16, 16*B*H*n for fp32, else
+ *              MEA_ERR_WORKSPACE), and attn_bwd_workspace_bytes(...) bytes for
+ *              the split backward on small grids; its contents on entry do not
+ *              matter and on return are unspecified. The part this call uses
+ *              (the row terms, or the whole split layout) must not overlap the
+ *              inputs or outputs.
  * Supported: dt in {MEA_DTYPE_BF16, MEA_DTYPE_F32} with d in {64, 128}. fp32
  * inputs form scores on fp64 MFMA and the exponent in fp64, as the forward
  * does; everything else is fp32.
@@ -166,9 +177,10 @@ MEA_API mea_status_t attn_fwd_ex(mea_dtype_t dt, int64_t B, int64_t H, int64_t H
                          void* o, float* row_max, float* row_sum, void* stream);
 
 /*
- * attn_bwd_ex_workspace_bytes - workspace attn_bwd_ex needs: 8*B*H*n_q
- * (bf16) or 16*B*H*n_q (fp32).
- * Returns 0 for empty or invalid shapes.
+ * attn_bwd_ex_workspace_bytes - workspace attn_bwd_ex is best given: the row
+ * terms, 8*B*H*n_q (bf16) or 16*B*H*n_q (fp32), which are the minimum, plus
+ * the split backward's partial gradients on small grids, as for
+ * attn_bwd_workspace_bytes. Returns 0 for empty or invalid shapes.
  */
 MEA_API size_t attn_bwd_ex_workspace_bytes(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv,
                                    int64_t n_q, int64_t n_k, int64_t d);

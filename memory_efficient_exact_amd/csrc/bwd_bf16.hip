@@ -103,6 +103,19 @@ struct BwdArgs {
   int total_q;    // dQ workgroups in the grid
   float C;        // log2(e) / sqrt(d)
   float scale;    // 1 / sqrt(d)
+  // split backward (small grids): each dK/dV workgroup position repeats for s_kv
+  // ranges of len_q staged query tiles, each dQ position for s_q ranges of len_k
+  // key tiles; a split side writes fp32 partials (before the 1/sqrt(d) factor)
+  // to Pdk, Pdv ([s_kv][kv_rows][D]) or Pdq ([s_q][q_rows][D]), else they are null
+  int s_kv;
+  int len_q;
+  int s_q;
+  int len_k;
+  float* Pdk;
+  float* Pdv;
+  float* Pdq;
+  int64_t kv_rows;  // heads * n_k
+  int64_t q_rows;   // heads * n_q
 };
 
 template <int D>
@@ -128,9 +141,10 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int wg, bf16* s0, bf
   const int n_q = a.n_q, n_k = a.n_k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int tile = xcd_remap(wg, a.total_kv);
-  const int bh = tile / a.tiles_kv;
-  const int kt = tile - bh * a.tiles_kv;
+  const int tile = xcd_remap(wg, a.total_kv);  // ((bh * s_kv) + sp) * tiles_kv + kt
+  const int bh = tile / (a.tiles_kv * a.s_kv);
+  const int sp = (tile - bh * a.tiles_kv * a.s_kv) / a.tiles_kv;  // range of query tiles
+  const int kt = tile - (bh * a.s_kv + sp) * a.tiles_kv;
   const int64_t qbase = (int64_t)bh * n_q * D;  // Q, dO (all query rows of the head)
   const int64_t kbase = (int64_t)bh * n_k * D;  // K, V, dK, dV
   const int64_t rbase = (int64_t)bh * n_q;
@@ -217,26 +231,48 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int wg, bf16* s0, bf
     }
   };
 
-  const int ntiles = (n_q + kTileQ - 1) / kTileQ;
+  // this workgroup's query tiles [t0, t1): all of them unless the backward is split
+  const int t0 = sp * a.len_q;
+  const int t1 = min(t0 + a.len_q, (n_q + kTileQ - 1) / kTileQ);
   auto step = [&](const bf16* qs, const bf16* os, const float* fs, bf16* qn, bf16* on, float* fn,
                   int t) {
     const int i0 = t * kTileQ;
-    if (t + 1 < ntiles) issue(qn, on, fn, i0 + kTileQ);
+    if (t + 1 < t1) issue(qn, on, fn, i0 + kTileQ);
     if (i0 + kTileQ <= n_q) tile_body(qs, os, fs, i0, std::false_type{});
     else tile_body(qs, os, fs, i0, std::true_type{});
     wait_all();
     __syncthreads();
   };
-  if (ntiles > 0) {  // no query rows at all: dK = dV = 0
-    issue(s0, s1, f0, 0);
+  if (t1 > t0) {  // no query rows at all: dK = dV = 0
+    issue(s0, s1, f0, t0 * kTileQ);
     wait_all();
     __syncthreads();
   }
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = t0; t < t1; t += 2) {
     step(s0, s1, f0, s2, s3, f1, t);
-    if (t + 1 < ntiles) step(s2, s3, f1, s0, s1, f0, t + 1);
+    if (t + 1 < t1) step(s2, s3, f1, s0, s1, f0, t + 1);
   }
 
+  if (a.Pdk != nullptr) {  // split: this range's fp32 partials, dK before its factor
+    if (key < n_k) {
+      const int64_t prow = (int64_t)sp * a.kv_rows * D + kbase + (int64_t)key * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int col = db * 32 + 8 * r4 + 4 * hi;
+          f32x4 pv, pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pv[e] = accV[db][4 * r4 + e];
+            pk[e] = accK[db][4 * r4 + e];
+          }
+          *reinterpret_cast<f32x4*>(a.Pdv + prow + col) = pv;
+          *reinterpret_cast<f32x4*>(a.Pdk + prow + col) = pk;
+        }
+    }
+    return;
+  }
   if (key < n_k) {
     bf16* vrow = a.dV + kbase + (int64_t)key * D;
     bf16* krow_out = a.dK + kbase + (int64_t)key * D;
@@ -271,9 +307,10 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int wg, bf16* s0, bf16
   const int n_q = a.n_q, n_k = a.n_k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int tile = xcd_remap(wg, a.total_q);
-  const int bh = tile / a.tiles_q;
-  const int qt = tile - bh * a.tiles_q;
+  const int tile = xcd_remap(wg, a.total_q);  // ((bh * s_q) + sp) * tiles_q + qt
+  const int bh = tile / (a.tiles_q * a.s_q);
+  const int sp = (tile - bh * a.tiles_q * a.s_q) / a.tiles_q;  // range of key tiles
+  const int qt = tile - (bh * a.s_q + sp) * a.tiles_q;
   const int64_t qbase = (int64_t)bh * n_q * D;  // Q, dO, dQ
   const int64_t kbase = (int64_t)bh * n_k * D;  // K, V
   const int row = qt * (32 * W) + wave * 32 + l32;  // this lane's query
@@ -338,10 +375,12 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int wg, bf16* s0, bf16
     }
   };
 
-  const int ntiles = (n_k + kTileK - 1) / kTileK;
+  // this workgroup's key tiles [t0, t1): all of them unless the backward is split
+  const int t0 = sp * a.len_k;
+  const int t1 = min(t0 + a.len_k, (n_k + kTileK - 1) / kTileK);
   auto step = [&](const bf16* ks, const bf16* vs, bf16* kn, bf16* vn, int t) {
     const int j0 = t * kTileK;
-    if (t + 1 < ntiles) {
+    if (t + 1 < t1) {
       dma.issue(a.K + kbase, j0 + kTileK, n_k, kn);
       dma.issue(a.V + kbase, j0 + kTileK, n_k, vn);
     }
@@ -350,15 +389,30 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int wg, bf16* s0, bf16
     wait_all();
     __syncthreads();
   };
-  dma.issue(a.K + kbase, 0, n_k, s0);
-  dma.issue(a.V + kbase, 0, n_k, s1);
+  dma.issue(a.K + kbase, t0 * kTileK, n_k, s0);
+  dma.issue(a.V + kbase, t0 * kTileK, n_k, s1);
   wait_all();
   __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = t0; t < t1; t += 2) {
     step(s0, s1, s2, s3, t);
-    if (t + 1 < ntiles) step(s2, s3, s0, s1, t + 1);
+    if (t + 1 < t1) step(s2, s3, s0, s1, t + 1);
   }
 
+  if (a.Pdq != nullptr) {  // split: this range's fp32 partial, before the 1/sqrt(d) factor
+    if (row < n_q) {
+      const int64_t prow = (int64_t)sp * a.q_rows * D + qbase + (int64_t)row * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f32x4 pq;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pq[e] = acc[db][4 * r4 + e];
+          *reinterpret_cast<f32x4*>(a.Pdq + prow + db * 32 + 8 * r4 + 4 * hi) = pq;
+        }
+    }
+    return;
+  }
   if (row < n_q) {
     bf16* qout = a.dQ + qbase + (int64_t)row * D;
 #pragma unroll
@@ -470,9 +524,10 @@ __device__ __forceinline__ void dkdv_role128(const BwdArgs& a, int wg, bf16* s0,
   const int n_q = a.n_q, n_k = a.n_k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int tile = xcd_remap(wg, a.total_kv);
-  const int bh = tile / a.tiles_kv;
-  const int kt = tile - bh * a.tiles_kv;
+  const int tile = xcd_remap(wg, a.total_kv);  // ((bh * s_kv) + sp) * tiles_kv + kt
+  const int bh = tile / (a.tiles_kv * a.s_kv);
+  const int sp = (tile - bh * a.tiles_kv * a.s_kv) / a.tiles_kv;  // range of query tiles
+  const int kt = tile - (bh * a.s_kv + sp) * a.tiles_kv;
   const int64_t qbase = (int64_t)bh * n_q * D;
   const int64_t kbase = (int64_t)bh * n_k * D;
   const int64_t rbase = (int64_t)bh * n_q;
@@ -555,26 +610,39 @@ __device__ __forceinline__ void dkdv_role128(const BwdArgs& a, int wg, bf16* s0,
     }
   };
 
-  const int ntiles = (n_q + kTileQ - 1) / kTileQ;
+  // this workgroup's query tiles [t0, t1): all of them unless the backward is split
+  const int t0 = sp * a.len_q;
+  const int t1 = min(t0 + a.len_q, (n_q + kTileQ - 1) / kTileQ);
   auto step = [&](const bf16* qs, const bf16* os, const float* fs, bf16* qn, bf16* on, float* fn,
                   int t) {
     const int i0 = t * kTileQ;
-    if (t + 1 < ntiles) issue(qn, on, fn, i0 + kTileQ);
+    if (t + 1 < t1) issue(qn, on, fn, i0 + kTileQ);
     if (i0 + kTileQ <= n_q) tile_body(qs, os, fs, i0, std::false_type{});
     else tile_body(qs, os, fs, i0, std::true_type{});
     wait_all();
     __syncthreads();
   };
-  if (ntiles > 0) {  // no query rows at all: dK = dV = 0
-    issue(s0, s1, f0, 0);
+  if (t1 > t0) {  // no query rows at all: dK = dV = 0
+    issue(s0, s1, f0, t0 * kTileQ);
     wait_all();
     __syncthreads();
   }
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = t0; t < t1; t += 2) {
     step(s0, s1, f0, s2, s3, f1, t);
-    if (t + 1 < ntiles) step(s2, s3, f1, s0, s1, f0, t + 1);
+    if (t + 1 < t1) step(s2, s3, f1, s0, s1, f0, t + 1);
   }
 
+  if (a.Pdk != nullptr) {  // split: this range's fp32 partials, dK before its factor
+    if (key < n_k) {
+      const int64_t prow = (int64_t)sp * a.kv_rows * D + kbase + (int64_t)key * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        *reinterpret_cast<f32x4*>(a.Pdv + prow + db * 16 + 4 * g) = accV[db];
+        *reinterpret_cast<f32x4*>(a.Pdk + prow + db * 16 + 4 * g) = accK[db];
+      }
+    }
+    return;
+  }
   if (key < n_k) {
     bf16* vrow = a.dV + kbase + (int64_t)key * D;
     bf16* krow_out = a.dK + kbase + (int64_t)key * D;
@@ -605,9 +673,10 @@ __device__ __forceinline__ void dq_role128(const BwdArgs& a, int wg, bf16* s0, b
   const int n_q = a.n_q, n_k = a.n_k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int tile = xcd_remap(wg, a.total_q);
-  const int bh = tile / a.tiles_q;
-  const int qt = tile - bh * a.tiles_q;
+  const int tile = xcd_remap(wg, a.total_q);  // ((bh * s_q) + sp) * tiles_q + qt
+  const int bh = tile / (a.tiles_q * a.s_q);
+  const int sp = (tile - bh * a.tiles_q * a.s_q) / a.tiles_q;  // range of key tiles
+  const int qt = tile - (bh * a.s_q + sp) * a.tiles_q;
   const int64_t qbase = (int64_t)bh * n_q * D;
   const int64_t kbase = (int64_t)bh * n_k * D;
   const int row = qt * (16 * W) + wave * 16 + l16;  // this lane's query
@@ -669,10 +738,12 @@ __device__ __forceinline__ void dq_role128(const BwdArgs& a, int wg, bf16* s0, b
     }
   };
 
-  const int ntiles = (n_k + kTileK - 1) / kTileK;
+  // this workgroup's key tiles [t0, t1): all of them unless the backward is split
+  const int t0 = sp * a.len_k;
+  const int t1 = min(t0 + a.len_k, (n_k + kTileK - 1) / kTileK);
   auto step = [&](const bf16* ks, const bf16* vs, bf16* kn, bf16* vn, int t) {
     const int j0 = t * kTileK;
-    if (t + 1 < ntiles) {
+    if (t + 1 < t1) {
       dma.issue(a.K + kbase, j0 + kTileK, n_k, kn);
       dma.issue(a.V + kbase, j0 + kTileK, n_k, vn);
     }
@@ -681,15 +752,24 @@ __device__ __forceinline__ void dq_role128(const BwdArgs& a, int wg, bf16* s0, b
     wait_all();
     __syncthreads();
   };
-  dma.issue(a.K + kbase, 0, n_k, s0);
-  dma.issue(a.V + kbase, 0, n_k, s1);
+  dma.issue(a.K + kbase, t0 * kTileK, n_k, s0);
+  dma.issue(a.V + kbase, t0 * kTileK, n_k, s1);
   wait_all();
   __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = t0; t < t1; t += 2) {
     step(s0, s1, s2, s3, t);
-    if (t + 1 < ntiles) step(s2, s3, s0, s1, t + 1);
+    if (t + 1 < t1) step(s2, s3, s0, s1, t + 1);
   }
 
+  if (a.Pdq != nullptr) {  // split: this range's fp32 partial, before the 1/sqrt(d) factor
+    if (row < n_q) {
+      const int64_t prow = (int64_t)sp * a.q_rows * D + qbase + (int64_t)row * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<f32x4*>(a.Pdq + prow + db * 16 + 4 * g) = acc[db];
+    }
+    return;
+  }
   if (row < n_q) {
     bf16* qout = a.dQ + qbase + (int64_t)row * D;
 #pragma unroll
@@ -715,6 +795,22 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_main128_kernel(BwdArgs a) {
   const int wg = blockIdx.x;
   if (wg < a.total_kv) dkdv_role128<W>(a, wg, s0, s1, s2, s3, f0, f1);
   else dq_role128<W>(a, wg - a.total_kv, s0, s1, s2, s3);
+}
+
+// Split fields of the kernel arguments; an unsplit side sweeps every tile.
+void set_split(BwdArgs& a, const BwdProblem& p) {
+  const bool kv = p.split.kv > 1, q = p.split.q > 1;
+  a.s_kv = kv ? p.split.kv : 1;
+  a.len_q = kv ? p.split.len_q : (p.rows_q + kTileQ - 1) / kTileQ;
+  a.s_q = q ? p.split.q : 1;
+  a.len_k = q ? p.split.len_k : (p.n_k + kTileK - 1) / kTileK;
+  a.Pdk = kv ? p.part_dk : nullptr;
+  a.Pdv = kv ? p.part_dv : nullptr;
+  a.Pdq = q ? p.part_dq : nullptr;
+  a.kv_rows = p.heads * p.n_k;
+  a.q_rows = p.heads * p.rows_q;
+  a.total_kv = (int)(p.heads * a.tiles_kv * a.s_kv);
+  a.total_q = (int)(p.heads * a.tiles_q * a.s_q);
 }
 
 template <int D, int W>
@@ -743,13 +839,14 @@ hipError_t launch(const BwdProblem& p, hipStream_t stream) {
   a.n_k = p.n_k;
   a.tiles_kv = (p.n_k + 32 * W - 1) / (32 * W);
   a.tiles_q = (p.rows_q + 32 * W - 1) / (32 * W);
-  a.total_kv = (int)(p.heads * a.tiles_kv);
-  a.total_q = (int)(p.heads * a.tiles_q);
+  set_split(a, p);
   a.scale = 1.0f / sqrtf((float)D);
   a.C = kLog2e * a.scale;
   hipLaunchKernelGGL((bwd_main_kernel<D, W>), dim3((unsigned)(a.total_kv + a.total_q)), dim3(64 * W),
                      0, stream, a);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_bwd_reduce(true, D, p, stream);
 }
 
 }  // namespace
@@ -781,13 +878,19 @@ hipError_t launch128(const BwdProblem& p, hipStream_t stream) {
   a.n_k = p.n_k;
   a.tiles_kv = (p.n_k + 16 * W - 1) / (16 * W);
   a.tiles_q = (p.rows_q + 16 * W - 1) / (16 * W);
-  a.total_kv = (int)(p.heads * a.tiles_kv);
-  a.total_q = (int)(p.heads * a.tiles_q);
+  set_split(a, p);
   a.scale = 1.0f / sqrtf((float)D);
   a.C = kLog2e * a.scale;
   hipLaunchKernelGGL((bwd_main128_kernel<W>), dim3((unsigned)(a.total_kv + a.total_q)),
                      dim3(64 * W), 0, stream, a);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_bwd_reduce(true, D, p, stream);
+}
+
+static_assert(kTileQ == kTileK, "one staged tile size for both roles");
+BwdGeometry bwd_geometry_bf16(int d) {
+  return BwdGeometry{(d == 64 ? 32 : 16) * kWaves, kTileQ};
 }
 
 hipError_t launch_bwd_bf16(int d, const BwdProblem& p, hipStream_t stream) {

@@ -105,6 +105,18 @@ struct BwdArgs32 {
   int total_q;
   double C64;    // log2(e) / sqrt(D)
   float scale;   // 1 / sqrt(D)
+  // split backward (small grids), as in the bf16 kernels: s_kv ranges of len_q
+  // query tiles per dK/dV position, s_q ranges of len_k key tiles per dQ
+  // position; a split side writes fp32 partials (before the 1/sqrt(d) factor)
+  int s_kv;
+  int len_q;
+  int s_q;
+  int len_k;
+  float* Pdk;      // [s_kv][kv_rows][D] or null
+  float* Pdv;
+  float* Pdq;      // [s_q][q_rows][D] or null
+  int64_t kv_rows;  // heads * n_k
+  int64_t q_rows;   // heads * n_q
 };
 
 template <int D>
@@ -149,15 +161,20 @@ __device__ __forceinline__ void dkdv_role32(const BwdArgs32& a, int wg, float* s
   constexpr int S = Shared32<D>::kStride;
   constexpr int KK = D / 4;   // k-steps over the head dimension
   constexpr int CB = D / 16;  // 16-column output blocks
-  const int n_q = a.n_q, n_k = a.n_k;
+  const int n_k = a.n_k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int tile = xcd_remap(wg, a.total_kv);
-  const int bh = tile / a.tiles_kv;
-  const int kt = tile - bh * a.tiles_kv;
-  const float* Qh = a.Q + (int64_t)bh * n_q * D;
-  const float* dOh = a.dO + (int64_t)bh * n_q * D;
-  const RowTerm* Th = a.T + (int64_t)bh * n_q;
+  const int tile = xcd_remap(wg, a.total_kv);  // ((bh * s_kv) + sp) * tiles_kv + kt
+  const int bh = tile / (a.tiles_kv * a.s_kv);
+  const int sp = (tile - bh * a.tiles_kv * a.s_kv) / a.tiles_kv;  // range of query tiles
+  const int kt = tile - (bh * a.s_kv + sp) * a.tiles_kv;
+  // this workgroup's query rows start at q_off (0 unless the backward is split); the
+  // sweep addresses them from there, so its loop keeps the unsplit form
+  const int q_off = sp * a.len_q * kTile;
+  const int n_q = a.n_q - q_off;  // query rows from the range's first on
+  const float* Qh = a.Q + ((int64_t)bh * a.n_q + q_off) * D;
+  const float* dOh = a.dO + ((int64_t)bh * a.n_q + q_off) * D;
+  const RowTerm* Th = a.T + (int64_t)bh * a.n_q + q_off;
   const int64_t kbase = (int64_t)bh * n_k * D;
   const int key = kt * kRows + wave * 16 + l16;  // this lane's key (column of S)
   const int krow = min(key, n_k - 1);
@@ -176,7 +193,7 @@ __device__ __forceinline__ void dkdv_role32(const BwdArgs32& a, int wg, float* s
     accK[cb] = f32x4{};
   }
 
-  const int ntiles = (n_q + kTile - 1) / kTile;
+  const int ntiles = min(a.len_q, (n_q + kTile - 1) / kTile);  // tiles of this range
   Stage<D> stQ, stO;
   RowTerm stT;
   auto gload = [&](int i0) {
@@ -237,13 +254,19 @@ __device__ __forceinline__ void dkdv_role32(const BwdArgs32& a, int wg, float* s
     __syncthreads();
   }
 
+  // outputs, or (split) this range's fp32 partials with dK before its factor: the
+  // same stores into other rows, chosen by workgroup-uniform values
+  const bool part = a.Pdk != nullptr;
+  float* vout_base = part ? a.Pdv + (int64_t)sp * a.kv_rows * D : a.dV;
+  float* kout_base = part ? a.Pdk + (int64_t)sp * a.kv_rows * D : a.dK;
+  const float kscale = part ? 1.0f : a.scale;
   if (key < n_k) {
-    float* vrow = a.dV + kbase + (int64_t)key * D;
-    float* krow_out = a.dK + kbase + (int64_t)key * D;
+    float* vrow = vout_base + kbase + (int64_t)key * D;
+    float* krow_out = kout_base + kbase + (int64_t)key * D;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       *reinterpret_cast<f32x4*>(vrow + 16 * cb + 4 * g4) = accV[cb];
-      *reinterpret_cast<f32x4*>(krow_out + 16 * cb + 4 * g4) = accK[cb] * a.scale;
+      *reinterpret_cast<f32x4*>(krow_out + 16 * cb + 4 * g4) = accK[cb] * kscale;
     }
   }
 }
@@ -254,15 +277,20 @@ __device__ __forceinline__ void dq_role32(const BwdArgs32& a, int wg, float* sK,
   constexpr int S = Shared32<D>::kStride;
   constexpr int KK = D / 4;
   constexpr int CB = D / 16;
-  const int n_q = a.n_q, n_k = a.n_k;
+  const int n_q = a.n_q;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int tile = xcd_remap(wg, a.total_q);
-  const int bh = tile / a.tiles_q;
-  const int qt = tile - bh * a.tiles_q;
+  const int tile = xcd_remap(wg, a.total_q);  // ((bh * s_q) + sp) * tiles_q + qt
+  const int bh = tile / (a.tiles_q * a.s_q);
+  const int sp = (tile - bh * a.tiles_q * a.s_q) / a.tiles_q;  // range of key tiles
+  const int qt = tile - (bh * a.s_q + sp) * a.tiles_q;
   const int64_t qbase = (int64_t)bh * n_q * D;
-  const float* Kh = a.K + (int64_t)bh * n_k * D;
-  const float* Vh = a.V + (int64_t)bh * n_k * D;
+  // this workgroup's keys start at k_off (0 unless the backward is split); the sweep
+  // addresses them from there, so its loop keeps the unsplit form
+  const int k_off = sp * a.len_k * kTile;
+  const int n_k = a.n_k - k_off;  // keys from the range's first on
+  const float* Kh = a.K + ((int64_t)bh * a.n_k + k_off) * D;
+  const float* Vh = a.V + ((int64_t)bh * a.n_k + k_off) * D;
   const int row = qt * kRows + wave * 16 + l16;  // this lane's query
   const int qrow = min(row, n_q - 1);
 
@@ -278,7 +306,7 @@ __device__ __forceinline__ void dq_role32(const BwdArgs32& a, int wg, float* sK,
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x4{};
 
-  const int ntiles = (n_k + kTile - 1) / kTile;
+  const int ntiles = min(a.len_k, (n_k + kTile - 1) / kTile);  // tiles of this range
   Stage<D> stK, stV;
   auto gload = [&](int j0) {
     stK.load(Kh, j0, n_k, tid);
@@ -328,11 +356,15 @@ __device__ __forceinline__ void dq_role32(const BwdArgs32& a, int wg, float* sK,
     __syncthreads();
   }
 
+  // the output, or (split) this range's fp32 partial before the 1/sqrt(d) factor
+  const bool part = a.Pdq != nullptr;
+  float* qout_base = part ? a.Pdq + (int64_t)sp * a.q_rows * D : a.dQ;
+  const float qscale = part ? 1.0f : a.scale;
   if (row < n_q) {
-    float* qout = a.dQ + qbase + (int64_t)row * D;
+    float* qout = qout_base + qbase + (int64_t)row * D;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
-      *reinterpret_cast<f32x4*>(qout + 16 * cb + 4 * g4) = acc[cb] * a.scale;
+      *reinterpret_cast<f32x4*>(qout + 16 * cb + 4 * g4) = acc[cb] * qscale;
   }
 }
 
@@ -370,16 +402,31 @@ hipError_t launch(const BwdProblem& p, hipStream_t stream) {
   a.n_k = p.n_k;
   a.tiles_kv = (p.n_k + kRows - 1) / kRows;
   a.tiles_q = (p.rows_q + kRows - 1) / kRows;
-  a.total_kv = (int)(p.heads * a.tiles_kv);
-  a.total_q = (int)(p.heads * a.tiles_q);
+  // split fields; an unsplit side sweeps every tile
+  const bool kv = p.split.kv > 1, q = p.split.q > 1;
+  a.s_kv = kv ? p.split.kv : 1;
+  a.len_q = kv ? p.split.len_q : (p.rows_q + kTile - 1) / kTile;
+  a.s_q = q ? p.split.q : 1;
+  a.len_k = q ? p.split.len_k : (p.n_k + kTile - 1) / kTile;
+  a.Pdk = kv ? p.part_dk : nullptr;
+  a.Pdv = kv ? p.part_dv : nullptr;
+  a.Pdq = q ? p.part_dq : nullptr;
+  a.kv_rows = p.heads * p.n_k;
+  a.q_rows = p.heads * p.rows_q;
+  a.total_kv = (int)(p.heads * a.tiles_kv * a.s_kv);
+  a.total_q = (int)(p.heads * a.tiles_q * a.s_q);
   a.scale = 1.0f / sqrtf((float)D);
   a.C64 = 1.4426950408889634 / sqrt((double)D);
   hipLaunchKernelGGL((bwd_main_f32_kernel<D>), dim3((unsigned)(a.total_kv + a.total_q)),
                      dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_bwd_reduce(false, D, p, stream);
 }
 
 }  // namespace
+
+BwdGeometry bwd_geometry_f32(int) { return BwdGeometry{kRows, kTile}; }
 
 hipError_t launch_bwd_f32(int d, const BwdProblem& p, hipStream_t stream) {
   if (d == 64) return launch<64>(p, stream);

@@ -72,6 +72,54 @@ mea_status_t check_shape(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int
 // keeps lse2 in fp64 (scores of ~1e4 need more than fp32 there) and -D.
 size_t bwd_row_bytes(bool bf16) { return bf16 ? 8 : 16; }
 
+// Split backward: grids of at most half the resident 4-wave workgroups (two
+// per CU) cut each workgroup's sweep into ranges of at least kBwdMinTiles
+// staged tiles, as many as keep the split grid within one round of resident
+// workgroups, at most kMaxBwdSplits.
+constexpr int64_t kMaxBwdSplits = 16;
+constexpr int64_t kBwdMinTiles = 2;
+
+mea::BwdSplit plan_bwd_split(const Shape& s) {
+  mea::BwdSplit p;
+  if (s.empty || s.rows_q == 0 || s.n_k == 0) return p;
+  const mea::BwdGeometry g = s.bf16 ? mea::bwd_geometry_bf16(s.d) : mea::bwd_geometry_f32(s.d);
+  const int64_t tiles_q = cdiv(s.rows_q, g.tile_rows), tiles_k = cdiv(s.n_k, g.tile_rows);
+  p.len_q = (int)tiles_q;
+  p.len_k = (int)tiles_k;
+  const int64_t base = s.heads * (cdiv(s.n_k, g.wg_rows) + cdiv(s.rows_q, g.wg_rows));
+  const int64_t want = std::min(kMaxBwdSplits, 2 * kComputeUnits / base);
+  if (want < 2) return p;
+  const int64_t len_q = std::min(tiles_q, std::max(kBwdMinTiles, cdiv(tiles_q, want)));
+  const int64_t len_k = std::min(tiles_k, std::max(kBwdMinTiles, cdiv(tiles_k, want)));
+  p.len_q = (int)len_q;
+  p.kv = (int)cdiv(tiles_q, len_q);  // every range non-empty
+  p.len_k = (int)len_k;
+  p.q = (int)cdiv(tiles_k, len_k);
+  return p;
+}
+
+// Backward workspace: the row terms, then (split sides only, from a 256-byte
+// boundary) fp32 partials of dK and dV [kv][heads * n_k][d] and of dQ
+// [q][heads * rows_q][d].
+struct BwdLayout {
+  mea::BwdSplit split;
+  size_t part_off = 0;  // bytes
+  size_t kv_part = 0;   // bytes of the dK partials (the dV partials follow)
+  size_t q_part = 0;
+  size_t total = 0;
+};
+
+BwdLayout bwd_layout(const Shape& s) {
+  BwdLayout L;
+  L.split = plan_bwd_split(s);
+  const size_t rows = bwd_row_bytes(s.bf16) * (size_t)s.q_rows_total;
+  L.part_off = (rows + 255) / 256 * 256;
+  if (L.split.kv > 1) L.kv_part = (size_t)L.split.kv * s.heads * s.n_k * s.d * 4;
+  if (L.split.q > 1) L.q_part = (size_t)L.split.q * s.heads * s.rows_q * s.d * 4;
+  L.total = (L.kv_part + L.q_part) > 0 ? L.part_off + 2 * L.kv_part + L.q_part : rows;
+  return L;
+}
+
 // Byte range [lo, hi) of one buffer of a call; empty ranges overlap nothing.
 struct Span {
   uintptr_t lo = 0;
@@ -202,11 +250,17 @@ mea_status_t bwd_impl(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_
   st = s.rows_q > 0 ? check_ptrs({q, k, v, o, dO, row_max, row_sum, dq, dk, dv})
                     : check_ptrs({k, v, dk, dv});
   if (st != MEA_OK) return st;
-  const size_t need = bwd_row_bytes(s.bf16) * (size_t)s.q_rows_total;
-  if (need > 0) {
-    if (workspace == nullptr || workspace_bytes < need) return MEA_ERR_WORKSPACE;
+  // The row terms are the minimum workspace. The split layout of a small grid
+  // needs the larger size that the workspace query reports; a workspace that
+  // holds only the row terms runs the unsplit backward.
+  const BwdLayout lay = bwd_layout(s);
+  const size_t min_need = bwd_row_bytes(s.bf16) * (size_t)s.q_rows_total;
+  if (min_need > 0) {
+    if (workspace == nullptr || workspace_bytes < min_need) return MEA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MEA_ERR_ALIGN;
   }
+  const bool split = lay.total > min_need && workspace_bytes >= lay.total;
+  const size_t need = split ? lay.total : min_need;  // bytes this call writes
   {
     const int64_t qb = q_bytes(s), kb = kv_bytes(s), sb = stat_bytes(s);
     st = check_alias({span(dq, qb), span(dk, kb), span(dv, kb), span(workspace, (int64_t)need)},
@@ -229,6 +283,15 @@ mea_status_t bwd_impl(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_
   p.dk = dk;
   p.dv = dv;
   p.ws = static_cast<float*>(workspace);
+  if (split) {
+    p.split = lay.split;
+    char* base = static_cast<char*>(workspace);
+    if (lay.kv_part > 0) {
+      p.part_dk = reinterpret_cast<float*>(base + lay.part_off);
+      p.part_dv = reinterpret_cast<float*>(base + lay.part_off + lay.kv_part);
+    }
+    if (lay.q_part > 0) p.part_dq = reinterpret_cast<float*>(base + lay.part_off + 2 * lay.kv_part);
+  }
   hipStream_t st_h = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = s.bf16 ? mea::launch_bwd_bf16(s.d, p, st_h) : mea::launch_bwd_f32(s.d, p, st_h);
   return e == hipSuccess ? MEA_OK : MEA_ERR_LAUNCH;
@@ -238,7 +301,7 @@ size_t bwd_ws_bytes(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_t 
                     int64_t d) {
   Shape s;
   if (check_shape(dt, B, H, H_kv, n_q, n_k, d, &s) != MEA_OK || s.empty) return 0;
-  return bwd_row_bytes(s.bf16) * (size_t)s.q_rows_total;
+  return bwd_layout(s).total;
 }
 
 }  // namespace

@@ -67,6 +67,29 @@ inline unsigned row_blocks(int64_t rows, int64_t rows_per_block) {
   return (unsigned)(b < kRowBlocks ? b : kRowBlocks);
 }
 
+// Split backward, for grids too small to fill the chip: the dK/dV workgroups
+// of a head are repeated for `kv` ranges of `len_q` staged query tiles each,
+// the dQ workgroups for `q` ranges of `len_k` key tiles. Where a side has more
+// than one range, each range writes fp32 partial sums (dK and dQ before their
+// 1/sqrt(d) factor) to the workspace, and a reduce pass sums them into the
+// outputs.
+// Unsplit: kv = q = 1 and the lengths cover every tile.
+struct BwdSplit {
+  int kv = 1;
+  int len_q = 0;
+  int q = 1;
+  int len_k = 0;
+};
+
+// Rows per 4-wave workgroup (keys of a dK/dV or queries of a dQ workgroup) and
+// rows per staged tile of the backward kernels, for planning the split.
+struct BwdGeometry {
+  int wg_rows;
+  int tile_rows;
+};
+BwdGeometry bwd_geometry_bf16(int d);
+BwdGeometry bwd_geometry_f32(int d);
+
 struct BwdProblem {
   int64_t heads = 0;  // B * H_kv
   int rows_q = 0;     // G * n_q
@@ -81,12 +104,22 @@ struct BwdProblem {
   void* dq = nullptr;
   void* dk = nullptr;  // [heads, n_k, d]: sums over the query heads of each group
   void* dv = nullptr;
-  float* ws = nullptr;  // row terms, bwd_workspace_per_row(dtype) bytes per query row
+  float* ws = nullptr;  // row terms: 8 (bf16) or 16 (fp32) bytes per query row
+  BwdSplit split;
+  // with split.kv > 1: [kv][heads * n_k][d] fp32 partials of dK and of dV;
+  // with split.q > 1: [q][heads * rows_q][d] fp32 partials of dQ (else null)
+  float* part_dk = nullptr;
+  float* part_dv = nullptr;
+  float* part_dq = nullptr;
 };
 
-// Backward: row preprocess, then one grid with dK/dV and dQ workgroups.
-// bf16: ws holds 2 floats per query row; fp32: 16 bytes per query row.
+// Backward: row preprocess, then one grid with dK/dV and dQ workgroups (and,
+// when split, the reduce pass). bf16: ws holds 2 floats per query row; fp32:
+// 16 bytes per query row.
 hipError_t launch_bwd_bf16(int d, const BwdProblem& p, hipStream_t stream);
 hipError_t launch_bwd_f32(int d, const BwdProblem& p, hipStream_t stream);
+// Sums the split partials of p into dK, dV (scaled by 1/sqrt(d)) and dQ (scaled),
+// in the output type; does nothing for a side that is not split.
+hipError_t launch_bwd_reduce(bool bf16, int d, const BwdProblem& p, hipStream_t stream);
 
 }  // namespace mea

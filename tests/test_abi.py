@@ -151,6 +151,16 @@ def test_outputs_must_not_overlap(L):
     # without query rows only dk, dv and the key side remain
     assert bwd_ex(L, n_q=0, ws=0, wsb=0, ptrs=dict(q=0, o=0, do=0, m=0, l=0, dq=0,
                                                    k=K, v=V, dk=K, dv=DV)) == ALIAS
+    # the split backward of a small grid writes its whole layout, but only when the
+    # workspace holds it: one head of 1024 rows, buffers 16 MiB apart
+    bq, bk, bv, bo, bd, bm, bl, bdq, bdk, bdv, bw = (A + (i << 24) for i in range(11))
+    full = mea.attn_bwd_workspace_bytes(BF16, 1, 1, 1024, 64)
+    assert full > 8 * 1024
+    sb = lambda wsb, **kw: bwd(L, n=1024, ws=bw, wsb=wsb, ptrs=dict(
+        dict(q=bq, k=bk, v=bv, o=bo, do=bd, m=bm, l=bl, dq=bdq, dk=bdk, dv=bdv), **kw))
+    assert sb(full, dq=bw + full - 16) == ALIAS      # the partials are written too
+    assert sb(full, dk=bw + 8 * 1024) == ALIAS
+    assert sb(8 * 1024, dq=bw + 8 * 1024 - 16) == ALIAS
     # split-key: 16384 keys make K and V 2 MiB each, so these buffers sit 16 MiB apart
     sq, sk, sv, so, sm, sl, sw = (A + (i << 24) for i in range(7))
     need = mea.attn_fwd_splitkv_workspace_bytes(BF16, 1, 1, 1, 1, 16384, 64, 0)
@@ -167,6 +177,39 @@ def test_workspace_bytes(L):
     assert mea.attn_bwd_workspace_bytes(BF16, 0, 8, 8192, 64) == 0
     assert mea.attn_bwd_workspace_bytes(BF16, 1, 1, 5, 96) == 0
     assert mea.attn_bwd_workspace_bytes(BF16, -1, 1, 5, 64) == 0
+
+
+def test_split_backward_workspace_bytes(L):
+    # Grids of at most 256 unsplit workgroups: the row terms, then from a 256-byte
+    # boundary the split's fp32 partials of dK and of dV ([ranges][B*H_kv*n_k][d]
+    # each) and of dQ ([ranges][B*H*n_q][d]); ranges = min(16, 512 // workgroups),
+    # each of at least two staged tiles.
+    ws = mea.attn_bwd_workspace_bytes
+    # bf16 d = 64: 128 rows per workgroup, 64-row tiles; one head of 1024 is 8 + 8
+    # workgroups and 16 tiles a side: 8 ranges of 2 tiles
+    assert ws(BF16, 1, 1, 1024, 64) == 8 * 1024 + 3 * 8 * 1024 * 64 * 4
+    # fp32 d = 64: 64 rows per workgroup, 32-row tiles: 16 + 16 workgroups, 16 ranges
+    assert ws(F32, 1, 1, 1024, 64) == 16 * 1024 + 3 * 16 * 1024 * 64 * 4
+    # 16 heads: 256 workgroups, two ranges of 8 tiles; 32 heads (512) are not split
+    assert ws(BF16, 1, 16, 1024, 64) == 8 * 16 * 1024 + 3 * 2 * 16 * 1024 * 64 * 4
+    assert ws(BF16, 1, 32, 1024, 64) == 8 * 32 * 1024
+    # bf16 d = 128: 64 rows per workgroup and per tile. The dK/dV workgroups sweep the
+    # stacked query rows of a group (4 x 300 = 1200), so their ranges cut the query
+    # tiles; the dQ workgroups sweep the keys, so theirs cut the key tiles.
+    exb = mea.attn_bwd_ex_workspace_bytes
+    k_tiles, q_tiles = 1000 // 64 + 1, 1200 // 64 + 1       # 16 and 19
+    wgs = 1 * (k_tiles + q_tiles)                            # 35 workgroups of 64 rows
+    r = min(16, 512 // wgs)                                  # 14
+    len_q, len_k = max(2, -(-q_tiles // r)), max(2, -(-k_tiles // r))
+    kv, q = -(-q_tiles // len_q), -(-k_tiles // len_k)       # 10 and 8
+    rows = 8 * 1200
+    off = -(-rows // 256) * 256
+    assert exb(BF16, 1, 4, 1, 300, 1000, 128) == off + 2 * kv * 1000 * 128 * 4 + q * 1200 * 128 * 4
+    # at most 32 MiB of partials whatever the small shape
+    for dt, d in ((BF16, 64), (BF16, 128), (F32, 64), (F32, 128)):
+        for n in (64, 300, 1024, 4096, 8192, 20000):
+            for H in (1, 2, 3, 8):
+                assert ws(dt, 1, H, n, d) - (8 if dt == BF16 else 16) * H * n <= 32 << 20 + 256
 
 
 def test_binding_rejects_cpu_and_mismatched_tensors():
@@ -344,7 +387,8 @@ int main(void) {
   if (attn_fwd_ex(MEA_DTYPE_F32, 1, 4, 3, 8, 8, 64, p, p, p, p, NULL, NULL, NULL) != MEA_ERR_SHAPE) return 3;
   if (attn_bwd(MEA_DTYPE_BF16, 0, 1, 8, 64, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
                NULL, NULL, 0, NULL) != MEA_OK) return 4;
-  if (attn_bwd_workspace_bytes(MEA_DTYPE_F32, 2, 8, 100, 128) != (size_t)16 * 2 * 8 * 100) return 5;
+  if (attn_bwd_workspace_bytes(MEA_DTYPE_F32, 2, 8, 8192, 128) != (size_t)16 * 2 * 8 * 8192) return 5;
+  if (attn_bwd_workspace_bytes(MEA_DTYPE_F32, 2, 8, 100, 128) <= (size_t)16 * 2 * 8 * 100) return 7;
   if (attn_fwd_splitkv_num_splits(MEA_DTYPE_BF16, 1, 32, 8, 1, 16384, 128, 0) < 2) return 6;
   printf("%s\n", attn_status_str(MEA_ERR_WORKSPACE));
   return 0;

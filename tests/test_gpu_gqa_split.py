@@ -312,6 +312,42 @@ def test_small_grid_decoding_layout_fp32_stress_full(d):
     check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, "fp32")
 
 
+# Split backward: on grids of at most 256 unsplit workgroups each workgroup's sweep
+# is cut into ranges whose fp32 partials a reduce pass sums, when the workspace
+# holds them (the size the workspace query reports). With only the row terms the
+# same call runs unsplit. Both are checked against the oracle and against each
+# other, with ragged tiles, grouped heads, both head dimensions and both types.
+SPLIT_BWD_CASES = [("bf16", 1, 1, 1, 1024, 1024, 64), ("bf16", 1, 3, 3, 700, 333, 64),
+                   ("bf16", 2, 4, 2, 300, 1000, 128), ("bf16", 1, 16, 16, 1024, 1024, 64),
+                   ("fp32", 1, 1, 1, 1024, 1024, 64), ("fp32", 1, 4, 1, 200, 777, 128),
+                   ("fp32", 2, 2, 2, 129, 1500, 64)]
+
+
+@pytest.mark.parametrize("dtype,B,H,H_kv,n_q,n_k,d", SPLIT_BWD_CASES)
+def test_split_backward_full(dtype, B, H, H_kv, n_q, n_k, d):
+    dt = mea.DTYPE_BF16 if dtype == "bf16" else mea.DTYPE_F32
+    row = 8 if dtype == "bf16" else 16
+    full = mea.attn_bwd_ex_workspace_bytes(dt, B, H, H_kv, n_q, n_k, d)
+    assert full > row * B * H * n_q  # the shape is split
+    say("split bwd", dtype, B, H, H_kv, n_q, n_k, d, full)
+    t = draw(B, H, H_kv, n_q, n_k, d, dtype, seed=201 + n_q + n_k + d, with_do=True)
+    q, k, v, do = (gpu(t[x]) for x in ("q", "k", "v", "do"))
+    o, m, l = mea.attn_fwd_ex(q, k, v)
+    ws_full = torch.empty(full, dtype=torch.uint8, device=q.device)
+    ws_min = torch.empty(row * B * H * n_q, dtype=torch.uint8, device=q.device)
+    s_dq, s_dk, s_dv = mea.attn_bwd_ex(q, k, v, o, do, m, l, workspace=ws_full)
+    u_dq, u_dk, u_dv = mea.attn_bwd_ex(q, k, v, o, do, m, l, workspace=ws_min)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.gqa_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]))
+    for name, got, ref in (("dQ", s_dq, rq), ("dK", s_dk, rk), ("dV", s_dv, rv),
+                           ("dQ unsplit", u_dq, rq), ("dK unsplit", u_dk, rk),
+                           ("dV unsplit", u_dv, rv)):
+        check(name, f64(got.cpu()), ref, dtype)
+    # split and unsplit differ only by the order of fp32 additions
+    for a, b in ((s_dq, u_dq), (s_dk, u_dk), (s_dv, u_dv)):
+        check("split vs unsplit", f64(a.cpu()), f64(b.cpu()), dtype)
+
+
 # The bf16 backward at d = 64 takes 8-wave workgroups (256 keys or queries each)
 # when heads x (key tiles + query tiles) of that size reach 256: ragged tiles on both
 # sides, grouped heads, and fewer keys than one workgroup covers.

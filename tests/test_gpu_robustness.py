@@ -153,9 +153,20 @@ def test_memory_overhead_is_linear(n):
     o, m, l = mea.attn_fwd(q, k, v)
     torch.cuda.synchronize()
     assert torch.cuda.max_memory_allocated() - base - io == 8 * B * H * n
-    dq, dk, dv = mea.attn_bwd(q, k, v, o, do, m, l)
+    # the minimum workspace: the 8-byte row terms (the split backward of small grids
+    # needs the larger size the workspace query reports, and is checked below)
+    ws = torch.empty(8 * B * H * n, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = mea.attn_bwd(q, k, v, o, do, m, l, workspace=ws)
     torch.cuda.synchronize()
     assert torch.cuda.max_memory_allocated() - base - 4 * io == 16 * B * H * n
+    del ws, dq, dk, dv
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    full = mea.attn_bwd_workspace_bytes(mea.DTYPE_BF16, B, H, n, d)
+    mea.attn_bwd(q, k, v, o, do, m, l)  # workspace allocated by the binding at that size
+    torch.cuda.synchronize()
+    assert torch.cuda.max_memory_allocated() - base - 4 * io == 8 * B * H * n + full
+    assert full - 8 * B * H * n <= (32 << 20) + 256  # split partials: bounded, small grids only
 
 
 def test_shared_inputs_and_adjacent_outputs():
