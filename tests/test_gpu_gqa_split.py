@@ -337,7 +337,10 @@ def test_split_backward_full(dtype, B, H, H_kv, n_q, n_k, d):
     ws_min = torch.empty(row * B * H * n_q, dtype=torch.uint8, device=q.device)
     s_dq, s_dk, s_dv = mea.attn_bwd_ex(q, k, v, o, do, m, l, workspace=ws_full)
     u_dq, u_dk, u_dv = mea.attn_bwd_ex(q, k, v, o, do, m, l, workspace=ws_min)
+    # one byte short of the split layout: the unsplit backward, bit for bit
+    c_dq, c_dk, c_dv = mea.attn_bwd_ex(q, k, v, o, do, m, l, workspace=ws_full[:full - 1])
     torch.cuda.synchronize()
+    assert torch.equal(c_dq, u_dq) and torch.equal(c_dk, u_dk) and torch.equal(c_dv, u_dv)
     rq, rk, rv = oracle.gqa_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]))
     for name, got, ref in (("dQ", s_dq, rq), ("dK", s_dk, rk), ("dV", s_dv, rv),
                            ("dQ unsplit", u_dq, rq), ("dK unsplit", u_dk, rk),
