@@ -35,6 +35,12 @@
 // No probability or score array is written to memory; dQ, dK and dV are each
 // written once by one workgroup, so results do not depend on scheduling.
 //
+// Split mode (grids of at most 256 workgroups, when the caller's workspace
+// holds it): each workgroup position repeats for several ranges of the tiles
+// it sweeps, each range writing fp32 partial sums to the workspace, and a
+// reduce pass (bwd_reduce.hip) adds the ranges in a fixed order; results are
+// again independent of scheduling.
+//
 // Grouped-query heads: the query heads sharing one key/value head arrive
 // stacked as the rows of one problem (see mea_launch.h), so a dK/dV workgroup
 // sweeps the query rows of the whole group and its dK, dV are the sums over

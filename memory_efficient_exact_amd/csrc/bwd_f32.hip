@@ -26,7 +26,10 @@
 //     wave's keys in registers) sweeping 32-row query tiles of Q, dO and the
 //     row terms staged in LDS; then dQ workgroups (64 queries, Q and dO in
 //     registers) sweeping 32-key tiles of K, V. Every output element is
-//     written once by one workgroup.
+//     written once by one workgroup. On grids of at most 256 workgroups, when
+//     the caller's workspace holds them, each workgroup position repeats for
+//     several ranges of its sweep and writes fp32 partial sums that a reduce
+//     pass (bwd_reduce.hip) adds in a fixed order.
 //
 // Occupancy. The register operands are held in fp32 and widened to fp64 at
 // each use (exact), and each tile goes through one LDS buffer, written
