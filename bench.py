@@ -344,6 +344,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shape", default=None,
+                    help="traffic mode only: run the step on B,H,n,d (bf16, seed 1003) instead "
+                         "of the default workload, e.g. 1,16,8192,128 for the d = 128 kernels")
     ap.add_argument("--mode", choices=("bench", "traffic", "configs", "splitkv", "memory"), default="bench",
                     help="traffic: one 256 MiB copy (counter calibration) and one step, "
                          "for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs; configs: time "
@@ -375,6 +378,11 @@ def main():
         print(json.dumps(sweep_memory()), flush=True)
         return
     w = inputgen.WORKLOADS["c3_long_bf16"]
+    if args.shape is not None:
+        if args.mode != "traffic":
+            ap.error("--shape applies to --mode traffic only")
+        B_, H_, n_, d_ = (int(x) for x in args.shape.split(","))
+        w = inputgen.Workload(f"shape_{B_}x{H_}x{n_}x{d_}", B_, H_, n_, d_, "bf16", seed=w.seed)
     t = inputgen.draw(w.B, w.H, w.n, w.d, w.dtype, seed=w.seed, with_do=True)
     q, k, v, do = (t[x].to(dev) for x in ("q", "k", "v", "do"))
     o = torch.empty_like(q)
