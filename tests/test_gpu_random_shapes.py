@@ -75,3 +75,32 @@ def test_random_shape(dtype, d, B, H, H_kv, n_q, n_k, mode, splits):
         check("dQ", f64(dq.cpu()), rq, dtype)
         check("dK", f64(dk.cpu()), rk, dtype)
         check("dV", f64(dv.cpu()), rv, dtype)
+
+
+def _large_cases(count=16, seed=4242):
+    # thousands of rows per head: the row-tiled, 8-wave and decoding layouts, split keys
+    # and the split backward all appear, with ragged lengths on both sides
+    rng = random.Random(seed)
+    out = []
+    while len(out) < count:
+        dtype = rng.choice(["bf16", "bf16", "fp32"])
+        d = rng.choice([64, 128])
+        B = rng.choice([1, 2])
+        H_kv = rng.choice([1, 2, 4, 8])
+        G = rng.choice([1, 2, 4])
+        n_q = rng.choice([511, 1000, 1537, 2048, 3001])
+        n_k = rng.choice([129, 1000, 2048, 3999])
+        mode = rng.choice(["fwd", "bwd", "split"])
+        case = (dtype, d, B, H_kv * G, H_kv, n_q, n_k, mode, 0 if mode == "split" else None)
+        if case not in out:
+            out.append(case)
+    return out
+
+
+LARGE_CASES = _large_cases()
+
+
+@pytest.mark.parametrize("dtype,d,B,H,H_kv,n_q,n_k,mode,splits", LARGE_CASES)
+def test_random_large_shape(dtype, d, B, H, H_kv, n_q, n_k, mode, splits):
+    test_random_shape(dtype, d, B, H, H_kv, n_q, n_k, mode, splits)
+
