@@ -22,7 +22,8 @@
  *    structure, no dropout. The score scale is fixed at 1/sqrt(d).
  *  - Every pointer is a DEVICE pointer on the current HIP device, owned by the
  *    caller, and must be 16-byte aligned. The library allocates no device
- *    memory and keeps no state between calls; it is thread-safe.
+ *    memory and keeps no state between calls (attn_bwd_noalloc aside, whose
+ *    scratch array is part of the loaded library); it is thread-safe.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
  *    the null stream). Nothing is synchronised. Inputs must stay valid and
  *    outputs untouched until the stream reaches the work.
@@ -153,6 +154,34 @@ MEA_API mea_status_t attn_bwd(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, i
                       const void* dO, const float* row_max, const float* row_sum,
                       void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/*
+ * attn_bwd_noalloc - attn_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments and errors as attn_bwd, minus
+ * the workspace, which is replaced by a scratch array inside the library.
+ *
+ * The scratch array holds MEA_NOALLOC_SCRATCH_BYTES (32 MiB). Each GPU the
+ * library runs on holds its own copy from the moment the library is loaded
+ * until the process ends; its device address is looked up on the first call
+ * made with that GPU current. The call needs the row terms of attn_bwd's
+ * workspace (8*B*H*n bytes for bf16, 16*B*H*n for fp32); larger shapes are
+ * rejected with MEA_ERR_WORKSPACE before anything runs. When the split layout
+ * of a small grid (see attn_bwd_workspace_bytes) also fits, it is used, and
+ * the results equal those of attn_bwd given that workspace, bit for bit;
+ * otherwise they equal attn_bwd given the row terms only.
+ * No memory is allocated and nothing needs clearing between calls: every byte
+ * a call reads from the scratch array it wrote first.
+ * Calls share their GPU's array: two calls that may run at the same time on
+ * one GPU (different streams, or different host threads without ordering)
+ * race on it and give undefined results. Calls ordered on one stream are safe.
+ * MEA_ERR_LAUNCH also reports a failure to look up the array's address.
+ */
+#define MEA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+MEA_API mea_status_t attn_bwd_noalloc(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d,
+                              const void* q, const void* k, const void* v, const void* o,
+                              const void* dO, const float* row_max, const float* row_sum,
+                              void* dq, void* dk, void* dv, void* stream);
 
 /*
  * attn_fwd_ex - forward pass with separate query/key lengths and shared

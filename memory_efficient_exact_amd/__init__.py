@@ -16,10 +16,13 @@ __all__ = [
     "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str", "mea_version",
     "attn_fwd_ex", "attn_bwd_ex", "attn_bwd_ex_workspace_bytes",
     "attn_fwd_splitkv", "attn_fwd_splitkv_num_splits", "attn_fwd_splitkv_workspace_bytes",
+    "attn_bwd_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+# size of the scratch array attn_bwd_noalloc runs in (MEA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _STATUS = ["MEA_OK", "MEA_ERR_NULL", "MEA_ERR_SHAPE", "MEA_ERR_UNSUPPORTED",
            "MEA_ERR_ALIGN", "MEA_ERR_WORKSPACE", "MEA_ERR_LAUNCH", "MEA_ERR_ALIAS"]
@@ -58,6 +61,8 @@ def lib():
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_bwd.argtypes = [i32, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.attn_bwd.restype = i32
+    L.attn_bwd_noalloc.argtypes = [i32, i64, i64, i64, i64] + [vp] * 11
+    L.attn_bwd_noalloc.restype = i32
     L.attn_fwd_ex.argtypes = [i32, i64, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
     L.attn_fwd_ex.restype = i32
     L.attn_bwd_ex_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i64, i64]
@@ -298,6 +303,31 @@ def attn_bwd(q, k, v, o, do, row_max, row_sum, dq=None, dk=None, dv=None, worksp
                _ptr(workspace), wbytes, _stream(stream, dev))
     if st != 0:
         raise MeaError("attn_bwd", st)
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, do, row_max, row_sum, dq, dk, dv, stream=None):
+    """``attn_bwd`` for callers that cannot allocate: no workspace argument (the
+    library runs in its own per-GPU scratch array of NOALLOC_SCRATCH_BYTES), and
+    the outputs dq, dk, dv must be passed, so the call allocates nothing.
+    Calls that may overlap on one GPU race on the scratch array."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, n, d]")
+    dt = _dtype_code(q)
+    di = q.get_device()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk),
+                    ("dv", dv)):
+        _check(name, t, q, di)
+    rows = q.shape[:3]
+    _check_stat("row_max", row_max, q, di, rows)
+    _check_stat("row_sum", row_sum, q, di, rows)
+    B, H, n, d = q.shape
+    dev = q.device
+    st = _call(dev, lib().attn_bwd_noalloc, dt, B, H, n, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+               _ptr(do), _ptr(row_max), _ptr(row_sum), _ptr(dq), _ptr(dk), _ptr(dv),
+               _stream(stream, dev))
+    if st != 0:
+        raise MeaError("attn_bwd_noalloc", st)
     return dq, dk, dv
 
 

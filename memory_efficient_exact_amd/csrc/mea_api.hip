@@ -1,17 +1,26 @@
 // C ABI of the library (declared in include/mea.h): argument validation on
 // the host, then dispatch to the gfx950 kernels on the caller's stream.
 // Validation never calls HIP, so every error path can be exercised without a
-// GPU. The library allocates nothing and keeps no state.
+// GPU. The library allocates nothing; its only state is the per-device address
+// of the scratch array that attn_bwd_noalloc uses.
 #include <algorithm>
 #include <climits>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/mea.h"
 #include "mea_launch.h"
 
+// Scratch memory of attn_bwd_noalloc: one array per GPU in the library's code
+// object, alive until the process ends. In host code `scratch` names a host-side
+// stand-in, not a device address: the address on each device comes from
+// hipGetSymbolAddress, looked up once per device (see noalloc_scratch below),
+// and only that address is ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MEA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
-constexpr int kVersion = 300;  // 0.3.0
+constexpr int kVersion = 400;  // 0.4.0
 // Grid bounds. With heads * ceil(max(rows_q, n_k) / 64) <= kMaxBlocks, the
 // tiled grids stay within 2^31 work-items: the largest give every 64 rows at
 // most two workgroups of 256 threads (the backward's dK/dV plus dQ workgroups
@@ -237,11 +246,38 @@ mea_status_t fwd_impl(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_
   return e == hipSuccess ? MEA_OK : MEA_ERR_LAUNCH;
 }
 
+// Device address of `scratch` on the current device: looked up with
+// hipGetSymbolAddress on the first call made with that device current, then
+// cached (each GPU holds its own copy of the array at its own address).
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// With use_scratch the caller's workspace arguments are ignored: the call runs
+// in the library's scratch array of MEA_NOALLOC_SCRATCH_BYTES (row terms, and the
+// split layout of a small grid whenever it fits), after the same validation.
 mea_status_t bwd_impl(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_t n_q,
                       int64_t n_k, int64_t d, const void* q, const void* k, const void* v,
                       const void* o, const void* dO, const float* row_max, const float* row_sum,
                       void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+                      void* stream, bool use_scratch = false) {
   Shape s;
   mea_status_t st = check_shape(dt, B, H, H_kv, n_q, n_k, d, &s);
   if (st != MEA_OK || s.empty) return st;
@@ -255,7 +291,12 @@ mea_status_t bwd_impl(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_
   // holds only the row terms runs the unsplit backward.
   const BwdLayout lay = bwd_layout(s);
   const size_t min_need = bwd_row_bytes(s.bf16) * (size_t)s.q_rows_total;
-  if (min_need > 0) {
+  if (use_scratch) {
+    // the scratch array is the workspace; it cannot overlap caller buffers
+    if (min_need > (size_t)MEA_NOALLOC_SCRATCH_BYTES) return MEA_ERR_WORKSPACE;
+    workspace = nullptr;
+    workspace_bytes = MEA_NOALLOC_SCRATCH_BYTES;
+  } else if (min_need > 0) {
     if (workspace == nullptr || workspace_bytes < min_need) return MEA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MEA_ERR_ALIGN;
   }
@@ -268,6 +309,7 @@ mea_status_t bwd_impl(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int64_
                       span(row_max, sb), span(row_sum, sb)});
     if (st != MEA_OK) return st;
   }
+  if (use_scratch && noalloc_scratch(&workspace) != hipSuccess) return MEA_ERR_LAUNCH;
   mea::BwdProblem p;
   p.heads = s.heads;
   p.rows_q = (int)s.rows_q;
@@ -361,6 +403,14 @@ mea_status_t attn_bwd_ex(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv, int
                          size_t workspace_bytes, void* stream) {
   return bwd_impl(dt, B, H, H_kv, n_q, n_k, d, q, k, v, o, dO, row_max, row_sum, dq, dk, dv,
                   workspace, workspace_bytes, stream);
+}
+
+mea_status_t attn_bwd_noalloc(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d,
+                              const void* q, const void* k, const void* v, const void* o,
+                              const void* dO, const float* row_max, const float* row_sum,
+                              void* dq, void* dk, void* dv, void* stream) {
+  return bwd_impl(dt, B, H, H, n, n, d, q, k, v, o, dO, row_max, row_sum, dq, dk, dv, nullptr, 0,
+                  stream, /*use_scratch=*/true);
 }
 
 int64_t attn_fwd_splitkv_num_splits(mea_dtype_t dt, int64_t B, int64_t H, int64_t H_kv,

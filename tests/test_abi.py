@@ -45,7 +45,7 @@ def test_exports_every_declared_symbol(L):
     assert set(names) >= {"attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
                           "mea_version", "attn_fwd_ex", "attn_bwd_ex", "attn_bwd_ex_workspace_bytes",
                           "attn_fwd_splitkv", "attn_fwd_splitkv_num_splits",
-                          "attn_fwd_splitkv_workspace_bytes"}
+                          "attn_fwd_splitkv_workspace_bytes", "attn_bwd_noalloc"}
     for nm in names:
         assert hasattr(L, nm), f"libmea.so does not export {nm}"
 
@@ -63,7 +63,7 @@ def test_status_strings(L):
                                  "MEA_ERR_ALIAS"]):
         assert mea.attn_status_str(code) == name
     assert mea.attn_status_str(99) == "MEA_UNKNOWN_STATUS"
-    assert mea.mea_version() == 300
+    assert mea.mea_version() == 400
 
 
 def fwd(L, dt=BF16, B=1, H=1, n=128, d=64, q=A, k=A, v=A, o=A, m=0, l=0):
@@ -122,6 +122,34 @@ def test_bwd_validation(L):
     assert bwd(L, wsb=8 * 128 - 1) == WS
     assert bwd(L, wsb=8 * 128, ws=A + 8) == ALIGN
     assert bwd(L, B=0, ws=0, wsb=0, ptrs={k: 0 for k in ("q", "k", "v")}) == OK
+
+
+def test_bwd_noalloc_validation(L):
+    # the backward without a workspace: same rules as attn_bwd, and the row terms
+    # (8 bytes per query row for bf16, 16 for fp32) must fit the 32 MiB scratch
+    # array. Every call below stops in validation (the pointers are fake).
+    assert mea.NOALLOC_SCRATCH_BYTES == 32 << 20
+    f = L.attn_bwd_noalloc
+
+    def call(dt=BF16, B=1, H=1, n=128, d=64, ptrs=None):
+        p = dict(zip(("q", "k", "v", "o", "do", "m", "l", "dq", "dk", "dv"), [A] * 10))
+        p.update(ptrs or {})
+        return f(dt, B, H, n, d, *p.values(), None)
+
+    assert call(dt=2) == UNSUP
+    assert call(d=96) == UNSUP
+    assert call(n=-1) == SHAPE
+    for name in ("q", "k", "v", "o", "do", "m", "l", "dq", "dk", "dv"):
+        assert call(ptrs={name: 0}) == NULL, name
+        assert call(ptrs={name: A + 4}) == ALIGN, name
+    rows = mea.NOALLOC_SCRATCH_BYTES // 8
+    assert call(n=rows + 1) == WS
+    assert call(H=2, n=rows // 2 + 1) == WS
+    assert call(dt=F32, n=rows // 2 + 1) == WS
+    # at the limit the size passes; these outputs overlap the inputs
+    assert call(n=rows) == ALIAS
+    assert call(dt=F32, n=rows // 2) == ALIAS
+    assert call(B=0, ptrs={"q": 0}) == OK
 
 
 # distinct fake buffers 1 MiB apart (every tensor below is far smaller)
@@ -382,7 +410,7 @@ int main(void) {
   char buf[16] __attribute__((aligned(16)));
   void* p = buf;
   /* validation paths only: no call below reaches a kernel launch */
-  if (mea_version() != 300) return 1;
+  if (mea_version() != 400) return 1;
   if (attn_fwd(MEA_DTYPE_BF16, 1, 1, 8, 96, p, p, p, p, NULL, NULL, NULL) != MEA_ERR_UNSUPPORTED) return 2;
   if (attn_fwd_ex(MEA_DTYPE_F32, 1, 4, 3, 8, 8, 64, p, p, p, p, NULL, NULL, NULL) != MEA_ERR_SHAPE) return 3;
   if (attn_bwd(MEA_DTYPE_BF16, 0, 1, 8, 64, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
