@@ -14,15 +14,21 @@
 // exponent would carry errors of ~1e-3). dP also runs on fp64 MFMA and D is
 // kept in fp64: dP - D cancels wherever P is concentrated (with a single key
 // it is exactly 0), and in fp32 the residue of that cancellation, summed over
-// many query rows into dK, reaches the tolerance. The weights, dS and the
-// three gradient products are fp32 (fp32 MFMA 16x16x4). lse2 = m*log2(e) +
-// log2(l) is formed per row in fp64 from the forward's statistics; the fp32
-// forward reports l relative to its reported (rounded) m, so the pair
-// reproduces the row's log-sum-exp to fp32 rounding of l alone.
+// many query rows into dK, reaches the tolerance. For the same reason D is not
+// taken from the caller's O (dO_i . O_i) but formed from the probabilities this
+// backward itself rebuilds, D_i = sum_j P_ij dP_ij / sum_j P_ij in fp64 (the D
+// pass below), so that every row of dS sums to zero; with D from an fp32 O the
+// rounding of O alone moved dQ by up to 7e-6 at the x30 stress scale. The
+// weights, dS and the three gradient products are fp32 (fp32 MFMA 16x16x4).
+// lse2 = m*log2(e) + log2(l) is formed per row in fp64 from the forward's
+// statistics; the fp32 forward reports l relative to its reported (rounded)
+// m, so the pair reproduces the row's log-sum-exp to fp32 rounding of l alone.
 //
-// Two launches on the caller's stream:
-//  1. bwd_rows_f32: per query row {lse2, -D} (both fp64) into the workspace.
-//  2. bwd_main_f32: dK/dV workgroups (64 keys, 16 per wave, K and V of the
+// Three launches on the caller's stream (the caller's O is not read):
+//  1. bwd_lse_f32: lse2 of every query row into the workspace (fp64).
+//  2. bwd_dterm_f32: -D of every query row (fp64), by a sweep over all keys of
+//     the row's head that forms S, dP and P as the main kernel does.
+//  3. bwd_main_f32: dK/dV workgroups (64 keys, 16 per wave, K and V of the
 //     wave's keys in registers) sweeping 32-row query tiles of Q, dO and the
 //     row terms staged in LDS; then dQ workgroups (64 queries, Q and dO in
 //     registers) sweeping 32-key tiles of K, V. Every output element is
@@ -61,33 +67,15 @@ struct RowTerm {
 static_assert(sizeof(RowTerm) == 16, "row term layout");
 
 // ------------------------------------------------------------ 1. row terms
-// One thread per (row, 4 columns); the D/4 threads of a row reduce by shuffles.
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_rows_f32_kernel(
-    const float* __restrict__ O, const float* __restrict__ dO, const float* __restrict__ Mx,
-    const float* __restrict__ Ls, RowTerm* __restrict__ terms, int64_t rows) {
-  constexpr int LPR = D / 4;
-  constexpr int RPB = kThreads / LPR;  // rows per workgroup and pass
-  const int part = threadIdx.x % LPR;
-  // workgroup-uniform stride over the rows (the grid may be capped)
-  for (int64_t r0 = (int64_t)blockIdx.x * RPB; r0 < rows; r0 += (int64_t)gridDim.x * RPB) {
-    const int64_t row = r0 + threadIdx.x / LPR;
-    double acc = 0.0;
-    if (row < rows) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(O + row * D + part * 4);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(dO + row * D + part * 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc = __builtin_fma((double)a[e], (double)b[e], acc);
-    }
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (row < rows && part == 0) {
-      RowTerm t;
-      t.lse2 = (double)Mx[row] * 1.4426950408889634 + log2((double)Ls[row]);
-      t.neg_d = -acc;
-      terms[row] = t;
-    }
-  }
+// One thread per query row: lse2 = m*log2(e) + log2(l) in fp64 from the forward's
+// statistics. The D pass below completes each row's term.
+__global__ __launch_bounds__(kThreads) void bwd_lse_f32_kernel(const float* __restrict__ Mx,
+                                                               const float* __restrict__ Ls,
+                                                               RowTerm* __restrict__ terms,
+                                                               int64_t rows) {
+  for (int64_t row = (int64_t)blockIdx.x * kThreads + threadIdx.x; row < rows;
+       row += (int64_t)gridDim.x * kThreads)
+    terms[row].lse2 = (double)Mx[row] * 1.4426950408889634 + log2((double)Ls[row]);
 }
 
 // ------------------------------------------------------------ 2. main kernel
@@ -106,8 +94,8 @@ struct BwdArgs32 {
   int tiles_q;   // dQ workgroups per head
   int total_kv;
   int total_q;
-  double C64;    // log2(e) / sqrt(D)
-  float scale;   // 1 / sqrt(D)
+  double C64;      // log2(e) / sqrt(D)
+  double scale64;  // 1 / sqrt(D)
   // split backward (small grids), as in the bf16 kernels: s_kv ranges of len_q
   // query tiles per dK/dV position, s_q ranges of len_k key tiles per dQ
   // position; a split side writes fp32 partials (before the 1/sqrt(d) factor)
@@ -189,11 +177,12 @@ __device__ __forceinline__ void dkdv_role32(const BwdArgs32& a, int wg, float* s
     kf[kk] = a.K[kbase + (int64_t)krow * D + 4 * kk + g4];
     vf[kk] = a.V[kbase + (int64_t)krow * D + 4 * kk + g4];
   }
-  f32x4 accV[CB], accK[CB];  // dV^T, dK^T: register r <-> column 16*cb + 4*g4 + r
+  // dV^T, dK^T accumulated in fp64 (fp64 MFMA): register r <-> column 16*cb + 4*r + g4
+  f64x4 accV[CB], accK[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    accV[cb] = f32x4{};
-    accK[cb] = f32x4{};
+    accV[cb] = f64x4{};
+    accK[cb] = f64x4{};
   }
 
   const int ntiles = min(a.len_q, (n_q + kTile - 1) / kTile);  // tiles of this range
@@ -244,8 +233,8 @@ __device__ __forceinline__ void dkdv_role32(const BwdArgs32& a, int wg, float* s
         const int q = 16 * qb + 4 * r + g4;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-          accV[cb] = mfma_f32_16x16x4(os[q * S + 16 * cb + l16], p[r], accV[cb]);
-          accK[cb] = mfma_f32_16x16x4(qs[q * S + 16 * cb + l16], ds[r], accK[cb]);
+          accV[cb] = mfma_f64_16x16x4((double)os[q * S + 16 * cb + l16], (double)p[r], accV[cb]);
+          accK[cb] = mfma_f64_16x16x4((double)qs[q * S + 16 * cb + l16], (double)ds[r], accK[cb]);
         }
       }
     }
@@ -262,15 +251,17 @@ __device__ __forceinline__ void dkdv_role32(const BwdArgs32& a, int wg, float* s
   const bool part = a.Pdk != nullptr;
   float* vout_base = part ? a.Pdv + (int64_t)sp * a.kv_rows * D : a.dV;
   float* kout_base = part ? a.Pdk + (int64_t)sp * a.kv_rows * D : a.dK;
-  const float kscale = part ? 1.0f : a.scale;
+  const double kscale = part ? 1.0 : a.scale64;
   if (key < n_k) {
     float* vrow = vout_base + kbase + (int64_t)key * D;
     float* krow_out = kout_base + kbase + (int64_t)key * D;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      *reinterpret_cast<f32x4*>(vrow + 16 * cb + 4 * g4) = accV[cb];
-      *reinterpret_cast<f32x4*>(krow_out + 16 * cb + 4 * g4) = accK[cb] * kscale;
-    }
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        vrow[16 * cb + 4 * r + g4] = (float)accV[cb][r];
+        krow_out[16 * cb + 4 * r + g4] = (float)(accK[cb][r] * kscale);
+      }
   }
 }
 
@@ -305,9 +296,9 @@ __device__ __forceinline__ void dq_role32(const BwdArgs32& a, int wg, float* sK,
     of[kk] = a.dO[qbase + (int64_t)qrow * D + 4 * kk + g4];
   }
   const RowTerm rt = a.T[(int64_t)bh * n_q + qrow];
-  f32x4 acc[CB];  // dQ^T: register r <-> column 16*cb + 4*g4 + r
+  f64x4 acc[CB];  // dQ^T in fp64 (fp64 MFMA): register r <-> column 16*cb + 4*r + g4
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x4{};
+  for (int cb = 0; cb < CB; ++cb) acc[cb] = f64x4{};
 
   const int ntiles = min(a.len_k, (n_k + kTile - 1) / kTile);  // tiles of this range
   Stage<D> stK, stV;
@@ -348,7 +339,8 @@ __device__ __forceinline__ void dq_role32(const BwdArgs32& a, int wg, float* sK,
       for (int r = 0; r < 4; ++r) {
         const int kr = 16 * kb + 4 * r + g4;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) acc[cb] = mfma_f32_16x16x4(ks[kr * S + 16 * cb + l16], ds[r], acc[cb]);
+        for (int cb = 0; cb < CB; ++cb)
+          acc[cb] = mfma_f64_16x16x4((double)ks[kr * S + 16 * cb + l16], (double)ds[r], acc[cb]);
       }
     }
     if (t + 1 < ntiles) {
@@ -362,17 +354,102 @@ __device__ __forceinline__ void dq_role32(const BwdArgs32& a, int wg, float* sK,
   // the output, or (split) this range's fp32 partial before the 1/sqrt(d) factor
   const bool part = a.Pdq != nullptr;
   float* qout_base = part ? a.Pdq + (int64_t)sp * a.q_rows * D : a.dQ;
-  const float qscale = part ? 1.0f : a.scale;
+  const double qscale = part ? 1.0 : a.scale64;
   if (row < n_q) {
     float* qout = qout_base + qbase + (int64_t)row * D;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
-      *reinterpret_cast<f32x4*>(qout + 16 * cb + 4 * g4) = acc[cb] * qscale;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) qout[16 * cb + 4 * r + g4] = (float)(acc[cb][r] * qscale);
   }
 }
 
+// ------------------------------------------------------------ 3. D pass
+// D_i = sum_j P_ij dP_ij / sum_j P_ij, with P_ij formed exactly as the main kernel
+// forms it (the same fp32 exp2 of the same fp64 exponent), accumulated in fp64.
+// Both sums run over every key of the row's head, so the main kernel's
+// dS_ij = P_ij (dP_ij - D_i) sums to zero over each row up to the fp32 rounding
+// of its terms. With D taken from the caller's O instead (dO_i . O_i, the same
+// number in exact arithmetic), the rounding of O enters dS through D alone:
+// where one key dominates a row (scores in the thousands), dS is a small
+// difference and dQ = dS K / sqrt(d) scales that error by |k| / sqrt(d)
+// (about 9 at the x30 stress scale, where even a correctly rounded fp32 O
+// costs 7e-6). Grid and sweep as the dQ role: 64 query rows per workgroup
+// (lane = query), 32-key tiles of K and V staged in LDS.
 template <int D>
-__global__ __launch_bounds__(kThreads, D == 128 ? 2 : 3) void bwd_main_f32_kernel(const BwdArgs32 a) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_dterm_f32_kernel(const BwdArgs32 a,
+                                                                     RowTerm* __restrict__ terms) {
+  constexpr int S = Shared32<D>::kStride;
+  constexpr int KK = D / 4;
+  __shared__ __attribute__((aligned(16))) float sK[Shared32<D>::kElems];
+  __shared__ __attribute__((aligned(16))) float sV[Shared32<D>::kElems];
+  const int n_q = a.n_q, n_k = a.n_k;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int tile = xcd_remap(blockIdx.x, (int)gridDim.x);  // bh * tiles_q + qt
+  const int bh = tile / a.tiles_q;
+  const int qt = tile - bh * a.tiles_q;
+  const int64_t qbase = (int64_t)bh * n_q * D;
+  const float* Kh = a.K + (int64_t)bh * n_k * D;
+  const float* Vh = a.V + (int64_t)bh * n_k * D;
+  const int row = qt * kRows + wave * 16 + l16;  // this lane's query
+  const int qrow = min(row, n_q - 1);
+  float qf[KK], of[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    qf[kk] = a.Q[qbase + (int64_t)qrow * D + 4 * kk + g4];
+    of[kk] = a.dO[qbase + (int64_t)qrow * D + 4 * kk + g4];
+  }
+  const double lse2 = a.T[(int64_t)bh * n_q + qrow].lse2;
+  double sum_p = 0.0, sum_pdp = 0.0;
+
+  const int ntiles = (n_k + kTile - 1) / kTile;
+  Stage<D> stK, stV;
+  stK.load(Kh, 0, n_k, tid);
+  stV.load(Vh, 0, n_k, tid);
+  stK.store(sK, tid);
+  stV.store(sV, tid);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * kTile;
+#pragma unroll
+    for (int kb = 0; kb < kTile / 16; ++kb) {
+      // S^T[key][q] and dP^T (fp64): lane holds query l16, register r <-> key 16kb + 4r + g4
+      f64x4 s = f64x4{}, dp = f64x4{};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int off = (16 * kb + l16) * S + 4 * kk + g4;
+        s = mfma_f64_16x16x4((double)sK[off], (double)qf[kk], s);
+        dp = mfma_f64_16x16x4((double)sV[off], (double)of[kk], dp);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float p = fast_exp2((float)(s[r] * a.C64 - lse2));
+        if (j0 + 16 * kb + 4 * r + g4 >= n_k) p = 0.f;  // padding keys
+        sum_p += (double)p;
+        sum_pdp = __builtin_fma((double)p, dp[r], sum_pdp);
+      }
+    }
+    if (t + 1 < ntiles) {
+      __syncthreads();
+      stK.load(Kh, j0 + kTile, n_k, tid);
+      stV.load(Vh, j0 + kTile, n_k, tid);
+      stK.store(sK, tid);
+      stV.store(sV, tid);
+    }
+    __syncthreads();
+  }
+  // the four lane groups g4 hold different keys of the same query
+#pragma unroll
+  for (int off = 16; off < 64; off <<= 1) {
+    sum_p += __shfl_xor(sum_p, off, 64);
+    sum_pdp += __shfl_xor(sum_pdp, off, 64);
+  }
+  if (row < n_q && g4 == 0) terms[(int64_t)bh * n_q + row].neg_d = -(sum_pdp / sum_p);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void bwd_main_f32_kernel(const BwdArgs32 a) {
   __shared__ __attribute__((aligned(16))) float s0[Shared32<D>::kElems];
   __shared__ __attribute__((aligned(16))) float s1[Shared32<D>::kElems];
   __shared__ __attribute__((aligned(16))) RowTerm sT[kTile];
@@ -385,13 +462,6 @@ template <int D>
 hipError_t launch(const BwdProblem& p, hipStream_t stream) {
   const int64_t rows = p.heads * p.rows_q;
   RowTerm* terms = reinterpret_cast<RowTerm*>(p.ws);
-  if (rows > 0) {
-    const unsigned blocks = row_blocks(rows, kThreads / (D / 4));
-    hipLaunchKernelGGL((bwd_rows_f32_kernel<D>), dim3(blocks), dim3(kThreads), 0, stream,
-                       (const float*)p.o, (const float*)p.dO, p.m, p.l, terms, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   BwdArgs32 a;
   a.Q = (const float*)p.q;
   a.K = (const float*)p.k;
@@ -418,8 +488,19 @@ hipError_t launch(const BwdProblem& p, hipStream_t stream) {
   a.q_rows = p.heads * p.rows_q;
   a.total_kv = (int)(p.heads * a.tiles_kv * a.s_kv);
   a.total_q = (int)(p.heads * a.tiles_q * a.s_q);
-  a.scale = 1.0f / sqrtf((float)D);
+  a.scale64 = 1.0 / sqrt((double)D);
   a.C64 = 1.4426950408889634 / sqrt((double)D);
+  if (rows > 0) {
+    // row terms: lse2 per row, then D from the rows' own probabilities
+    hipLaunchKernelGGL(bwd_lse_f32_kernel, dim3(row_blocks(rows, kThreads)), dim3(kThreads), 0,
+                       stream, p.m, p.l, terms, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dterm_f32_kernel<D>), dim3((unsigned)(p.heads * a.tiles_q)),
+                       dim3(kThreads), 0, stream, a, terms);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((bwd_main_f32_kernel<D>), dim3((unsigned)(a.total_kv + a.total_q)),
                      dim3(kThreads), 0, stream, a);
   const hipError_t e = hipGetLastError();

@@ -3,7 +3,11 @@
 // workspace, applies the 1/sqrt(d) factor of dK and dQ, and writes the
 // outputs in the input type. The gradients are sums over keys (dQ) or over
 // query rows (dK, dV), so splitting those sums into ranges and adding the
-// range totals gives the same result up to the order of fp32 additions.
+// range totals gives the same result up to rounding. The range totals are
+// added and scaled in fp64 and rounded once to the output type: where many
+// query rows share few keys, a key's dV or dK is a sum of hundreds of terms of
+// one sign (|dV| ~ 65 for 600 rows on one key) and fp32 additions of the range
+// totals alone would cost about one fp32 ulp of that magnitude (7.6e-6).
 //
 // HBM-bound: per output row S * d * 4 bytes read and d * sizeof(T) written.
 // One thread per 4 columns; the grid is capped and strides over the rows.
@@ -42,15 +46,21 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(const ReduceArgs a
       const int64_t row = r0 + threadIdx.x / CPR;
       if (row >= jb.rows) continue;
       const float* src = jb.part + row * D + c * 4;
-      f32x4 sum = *reinterpret_cast<const f32x4*>(src);
-      for (int s = 1; s < jb.splits; ++s) sum += *reinterpret_cast<const f32x4*>(src + s * stride);
-      sum *= jb.scale;
+      double sum[4] = {0.0, 0.0, 0.0, 0.0};
+      for (int s = 0; s < jb.splits; ++s) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(src + s * stride);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum[e] += (double)x[e];
+      }
+      f32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = (float)(sum[e] * (double)jb.scale);
       if constexpr (std::is_same<T, float>::value) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(jb.out) + row * D + c * 4) = sum;
+        *reinterpret_cast<f32x4*>(static_cast<float*>(jb.out) + row * D + c * 4) = r;
       } else {
         bf16x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (bf16)sum[e];
+        for (int e = 0; e < 4; ++e) o[e] = (bf16)r[e];
         *reinterpret_cast<bf16x4*>(static_cast<bf16*>(jb.out) + row * D + c * 4) = o;
       }
     }

@@ -1,18 +1,23 @@
 """GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
 
 Tolerances (max |gpu - oracle| per element, separately for O, dQ, dK, dV):
-  * fp32 inputs: 1e-5;
-  * bf16 inputs: 2e-2, and additionally relative L2 error <= 1e-2 (bf16
-    outputs are small, |O| <~ 0.1 at n >= 4096, so 2e-2 alone would admit
-    a badly wrong kernel).
-Both bars are absolute for outputs of magnitude <= 1 (every workload) and
-scale with max |reference| beyond that (see ``check``).
-Small shapes are compared in full; the full-size workloads are compared on
-sampled query rows (and sampled key rows for dK/dV), which the oracle
-computes exactly from the complete key set.
+  * fp32 inputs: 1e-5, absolute, for every element;
+  * bf16 inputs: 2e-2 absolute, or one bf16 ulp of the reference value where
+    that is larger (only |ref| >= 4, which no workload reaches: an output in
+    bf16 can be no closer than one of the two bf16 neighbours of the exact
+    value), and additionally relative L2 error <= 1e-2 (bf16 outputs are
+    small, |O| <~ 0.1 at n >= 4096, so 2e-2 alone would admit a badly wrong
+    kernel).
+Every element of every workload is compared, forward and backward; the
+oracle runs per (batch, head) on a thread pool to keep the full sizes within
+a minute or two of host time. With MEA_PARITY_RECORD=<path> set, every check
+appends its error figures to that file as one JSON line.
 """
 
+import json
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -48,20 +53,45 @@ def run_fwd(t):
     return o, m, l
 
 
-def check(name, got, ref, dtype):
+def ulp(x, dtype):
+    """Spacing of the output type at |x|: 2^(e - 7) for bf16 (8 significant
+    bits), 2^(e - 23) for fp32, with e = floor(log2 |x|); the smallest normal
+    spacing below that."""
+    a = np.abs(np.asarray(x, np.float64))
+    bits = 8 if dtype == "bf16" else 24
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return 2.0 ** (e - (bits - 1))
+
+
+def bar_of(ref, dtype):
+    """Per-element bar: 1e-5 for fp32; for bf16 the larger of 2e-2 and one bf16
+    ulp of the reference value (representability: the exact result lies
+    between two bf16 neighbours, which are one ulp apart)."""
+    if dtype == "fp32":
+        return np.full(np.shape(ref), TOL["fp32"])
+    return np.maximum(TOL["bf16"], ulp(ref, "bf16"))
+
+
+def record(entry):
+    path = os.environ.get("MEA_PARITY_RECORD")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(entry) + "\n")
+
+
+def check(name, got, ref, dtype, tag=None):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{name}: non-finite output"
-    err = np.abs(got - ref).max() if got.size else 0.0
-    # The bar is absolute for outputs of magnitude <= 1, which holds for every
-    # workload (bf16: |O|, |dQ|, |dK|, |dV| <~ 0.2). Where a test shape has
-    # larger outputs (one key shared by hundreds of query rows sums their dO
-    # into dV), an output in the input type cannot be closer than half its
-    # ulp, so the bar scales with the largest reference value.
-    bar = TOL[dtype] * max(1.0, float(np.abs(ref).max()) if ref.size else 0.0)
-    assert err <= bar, f"{name}: max abs err {err:.3e} > {bar:.3e}"
-    if dtype == "bf16" and got.size:
+    if not got.size:
+        return 0.0
+    diff = np.abs(got - ref)
+    err = float(diff.max())
+    bar = bar_of(ref, dtype)
+    worst = int(np.argmax(diff - bar))
+    rel = None
+    if dtype == "bf16":
         # relative L2, with a floor of 1e-3 rms on the denominator. An exactly
         # zero reference (dQ at n = 1; dK with a single key, where dP - D
         # vanishes) leaves only fp32 rounding noise of the order of 1e-6 (the
@@ -69,8 +99,38 @@ def check(name, got, ref, dtype):
         # becoming an unbounded ratio. It lies below every output scale of
         # the workloads (rms |O| >= 0.014 at n = 16384, rms dQ/dK/dV ~ 0.018).
         den = max(np.linalg.norm(ref), 1e-3 * math.sqrt(ref.size))
-        rel = np.linalg.norm(got - ref) / den
+        rel = float(np.linalg.norm(got - ref) / den)
+    if tag is not None:
+        record({"case": tag, "output": name, "dtype": dtype, "elements": int(ref.size),
+                "max_abs_err": err, "max_abs_ref": float(np.abs(ref).max()),
+                "bar": float(bar.max()) if dtype == "bf16" else TOL["fp32"],
+                "rel_l2": rel if rel is not None else float(
+                    np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))})
+    assert diff.flat[worst] <= bar.flat[worst], (
+        f"{name}: abs err {diff.flat[worst]:.3e} > bar {bar.flat[worst]:.3e} at flat index "
+        f"{worst} (ref {ref.flat[worst]:.6g}, got {got.flat[worst]:.6g}); max abs err {err:.3e}")
+    if rel is not None:
         assert rel <= REL_L2_BF16, f"{name}: rel L2 {rel:.3e}"
+    return err
+
+
+def check_relative(name, got, ref, dtype):
+    """The bf16 bar taken relative to the tensor's largest reference value,
+    2e-2 * max(1, max |ref|), plus the relative L2 gate: only for shapes whose
+    outputs lie far above the workloads' scale and where bf16 operands alone
+    cannot meet the absolute bar (each use says why)."""
+    assert dtype == "bf16"
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape and np.all(np.isfinite(got)), name
+    if not got.size:
+        return 0.0
+    err = float(np.abs(got - ref).max())
+    bar = TOL["bf16"] * max(1.0, float(np.abs(ref).max()))
+    assert err <= bar, f"{name}: max abs err {err:.3e} > {bar:.3e}"
+    den = max(np.linalg.norm(ref), 1e-3 * math.sqrt(ref.size))
+    rel = float(np.linalg.norm(got - ref) / den)
+    assert rel <= REL_L2_BF16, f"{name}: rel L2 {rel:.3e}"
     return err
 
 
@@ -134,9 +194,9 @@ def test_bwd_fp32_single_head_workload_full():
     dq, dk, dv = mea.attn_bwd(q, k, v, o, do, m, l)
     torch.cuda.synchronize()
     rq, rk, rv = oracle.naive_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]))
-    check("dQ", f64(dq.cpu()), rq, "fp32")
-    check("dK", f64(dk.cpu()), rk, "fp32")
-    check("dV", f64(dv.cpu()), rv, "fp32")
+    check("dQ", f64(dq.cpu()), rq, "fp32", tag=w.name + " backward")
+    check("dK", f64(dk.cpu()), rk, "fp32", tag=w.name + " backward")
+    check("dV", f64(dv.cpu()), rv, "fp32", tag=w.name + " backward")
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -153,9 +213,10 @@ def test_bwd_fp32_stress_scores(d):
     torch.cuda.synchronize()
     assert float(m.abs().max()) > 300.0
     rq, rk, rv = oracle.naive_bwd(f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"]))
-    check("dQ", f64(dq.cpu()), rq, "fp32")
-    check("dK", f64(dk.cpu()), rk, "fp32")
-    check("dV", f64(dv.cpu()), rv, "fp32")
+    tag = f"fp32 stress backward 1x2x1500x{d}"
+    check("dQ", f64(dq.cpu()), rq, "fp32", tag=tag)
+    check("dK", f64(dk.cpu()), rk, "fp32", tag=tag)
+    check("dV", f64(dv.cpu()), rv, "fp32", tag=tag)
 
 
 # ------------------------------------------------------------ invariants on GPU output
@@ -235,25 +296,38 @@ def test_gradient_sum_identities_on_gpu():
 
 # ------------------------------------------------------------ full-size workloads
 
-def sample_rows(n, count, seed):
-    rng = np.random.default_rng(seed)
-    fixed = np.array([0, 1, n // 2, n - 2, n - 1])
-    return np.unique(np.concatenate([fixed, rng.choice(n, size=count, replace=False)]))
+def oracle_heads(fn, *arrays, **kw):
+    """fn(*[a[b, h] for a in arrays], **kw) for every (b, h) of [B, H, n, d]
+    arrays, on a pool of host threads (one BLAS thread each; numpy releases the
+    interpreter lock in its matrix products and elementwise loops). Returns the
+    per-head results stacked back to [B, H, ...], one array per output of fn."""
+    from threadpoolctl import threadpool_limits
+    B, H = arrays[0].shape[:2]
+    jobs = [(b, h) for b in range(B) for h in range(H)]
+    workers = max(1, min(len(jobs), 16, len(os.sched_getaffinity(0))))
+    with threadpool_limits(limits=1), ThreadPoolExecutor(workers) as ex:
+        res = list(ex.map(lambda bh: fn(*(a[bh[0], bh[1]] for a in arrays), **kw), jobs))
+    outs = []
+    for i in range(len(res[0])):
+        stacked = np.stack([r[i] for r in res])
+        outs.append(stacked.reshape((B, H) + stacked.shape[1:]))
+    return outs
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["c1_single_head_fp32", "c2_multihead_bf16", "c3_long_bf16",
                                   "c4_stress_fp32"])
 def test_workload_forward(name):
+    # every query row of every head against the oracle's definition
     w = inputgen.WORKLOADS[name]
     say("workload fwd", name)
     t = inputgen.make_inputs(w)
     o, m, l = run_fwd(t)
     o, m, l = f64(o.cpu()), m.cpu().numpy(), l.cpu().numpy()
-    rows = np.arange(w.n) if w.n <= 1024 else sample_rows(w.n, 96, w.seed)
     q, k, v = f64(t["q"]), f64(t["k"]), f64(t["v"])
-    o_ref, m_ref, l_ref = oracle.naive_fwd(q, k, v, rows=rows)
-    err = check("O", o[:, :, rows], o_ref, w.dtype)
-    check_stats(m[:, :, rows], l[:, :, rows], m_ref, l_ref, w.dtype)
+    o_ref, m_ref, l_ref = oracle_heads(oracle.naive_fwd, q, k, v, row_block=512)
+    err = check("O", o, o_ref, w.dtype, tag=name)
+    check_stats(m, l, m_ref, l_ref, w.dtype)
     say(name, "max abs err", f"{err:.3e}")
     if w.equal_key_heads:
         # every query in an all-equal-key head gets the mean of the values
@@ -262,7 +336,9 @@ def test_workload_forward(name):
             check("O equal-key head", o[:, h], np.broadcast_to(mean, o[:, h].shape), w.dtype)
 
 
+@pytest.mark.timeout(900)
 def test_workload_training_step():
+    # 2 x 8 x 8192 x 64 bf16: O, dQ, dK and dV, every element
     w = inputgen.WORKLOADS["c5_train_bf16"]
     say("workload fwd+bwd", w.name)
     t = inputgen.make_inputs(w)
@@ -271,17 +347,14 @@ def test_workload_training_step():
     dq, dk, dv = mea.attn_bwd(q, k, v, o, do, m, l)
     torch.cuda.synchronize()
     o, dq, dk, dv = (f64(x.cpu()) for x in (o, dq, dk, dv))
-    rows = sample_rows(w.n, 48, w.seed)
-    cols = sample_rows(w.n, 48, w.seed + 1)
-    for b, h in ((0, 0), (1, 7)):
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        qs, ks, vs, dos = (f64(t[x])[sl] for x in ("q", "k", "v", "do"))
-        o_ref, _, _ = oracle.naive_fwd(qs, ks, vs, rows=rows)
-        check("O", o[sl][:, :, rows], o_ref, "bf16")
-        rq, rk, rv = oracle.naive_bwd(qs, ks, vs, dos, rows=rows, cols=cols)
-        check("dQ", dq[sl][:, :, rows], rq, "bf16")
-        check("dK", dk[sl][:, :, cols], rk, "bf16")
-        check("dV", dv[sl][:, :, cols], rv, "bf16")
+    q64, k64, v64, do64 = (f64(t[x]) for x in ("q", "k", "v", "do"))
+    o_ref, m_ref, l_ref = oracle_heads(oracle.naive_fwd, q64, k64, v64, row_block=512)
+    check("O", o, o_ref, "bf16", tag=w.name)
+    check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, "bf16")
+    rq, rk, rv = oracle_heads(oracle.naive_bwd, q64, k64, v64, do64, row_block=512)
+    for nm, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        err = check(nm, got, ref, "bf16", tag=w.name)
+        say(w.name, nm, "max abs err", f"{err:.3e}")
 
 
 def test_forward_allocates_nothing_beyond_outputs():
@@ -302,9 +375,11 @@ def test_forward_allocates_nothing_beyond_outputs():
     assert m.numel() * 4 + l.numel() * 4 == 8 * w.B * w.H * w.n
 
 
+@pytest.mark.timeout(900)
 def test_bench_step_workload_backward():
     # the step bench.py times: 1 x 16 x 16384 x 64 bf16, inputs drawn exactly as the bench
-    # draws them, forward with statistics then backward with a caller workspace
+    # draws them, forward with statistics then backward with a caller workspace; every
+    # element of dQ, dK and dV against the oracle
     w = inputgen.WORKLOADS["c3_long_bf16"]
     say("bench step fwd+bwd", w.name)
     t = inputgen.draw(w.B, w.H, w.n, w.d, w.dtype, seed=w.seed, with_do=True)
@@ -318,19 +393,11 @@ def test_bench_step_workload_backward():
     dq, dk, dv = mea.attn_bwd(q, k, v, o, do, m, l, workspace=ws)
     torch.cuda.synchronize()
     dq, dk, dv = (f64(x.cpu()) for x in (dq, dk, dv))
-    rows = sample_rows(w.n, 24, w.seed + 2)
-    cols = sample_rows(w.n, 24, w.seed + 3)
     q64, k64, v64, do64 = (f64(t[x]) for x in ("q", "k", "v", "do"))
-    # dQ rows on every head (each row needs only its own softmax)
-    rq, _, _ = oracle.naive_bwd(q64, k64, v64, do64, rows=rows, cols=np.array([], dtype=np.int64),
-                                row_block=64)
-    check("dQ", dq[:, :, rows], rq, "bf16")
-    # dK, dV key rows on two heads (every query row contributes)
-    for h in (0, 11):
-        sl = (slice(0, 1), slice(h, h + 1))
-        _, rk, rv = oracle.naive_bwd(q64[sl], k64[sl], v64[sl], do64[sl], rows=rows[:1], cols=cols)
-        check("dK", dk[sl][:, :, cols], rk, "bf16")
-        check("dV", dv[sl][:, :, cols], rv, "bf16")
+    rq, rk, rv = oracle_heads(oracle.naive_bwd, q64, k64, v64, do64, row_block=512)
+    for nm, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        err = check(nm, got, ref, "bf16", tag="c3_long_bf16 backward")
+        say("bench step", nm, "max abs err", f"{err:.3e}")
     # identities on every head: sum_j dK_j = 0, sum_j dV_j = sum_i dO_i
     for h in range(w.H):
         sk = np.abs(dk[0, h]).sum(axis=0)

