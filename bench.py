@@ -29,25 +29,18 @@ METRIC = "attention fwd/bwd TFLOP/s at n=16384 bf16 on 1 MI355X; % MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0
 COPY_BYTES = 256 << 20
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_bwd_main_n16384_bf16.md")
-KERNEL_SOURCE = os.path.join(ROOT, "memory_efficient_exact_amd", "csrc", "bwd_bf16.hip")
+DOMINANT_KERNEL = "bwd_main_kernel<64, 8>"
 
 
-def recorded_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None when the kernel source changed since it was taken."""
-    import hashlib
-    import re
+def recorded_figures(kernel):
+    """Counter figures of `kernel` from the committed rocprofv3 summaries under
+    profiles/ (HBM bytes per launch, MFMA busy, ...), or {} when its source changed
+    since they were taken."""
+    from memory_efficient_exact_amd import rocprof
     try:
-        text = open(TRAFFIC_SUMMARY).read()
-        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
-    except OSError:
-        return None
-    h = re.search(r"source sha256: ([0-9a-f]{64})", text)
-    b = re.search(r"HBM bytes per launch: ([0-9.e+]+)", text)
-    if not h or not b or h.group(1) != src:
-        return None
-    return float(b.group(1))
+        return rocprof.current_figures(os.path.join(ROOT, "profiles"), kernel)
+    except (OSError, ValueError, KeyError):
+        return {}
 
 
 def log(*a):
@@ -339,6 +332,49 @@ def sweep_memory():
     return {"mode": "memory", "rows": rows}
 
 
+def _traffic_program(shape):
+    return "python3 " + os.path.join(ROOT, "bench.py") + " --mode traffic" + (
+        f" --shape {shape}" if shape else "")
+
+
+def profile_tools(args):
+    """profile-plan: the rocprofv3 commands (one per pass); summarize: their reduction."""
+    from memory_efficient_exact_amd import rocprof
+    if not args.prof_dir:
+        sys.exit("--prof-dir is required")
+    program = _traffic_program(args.shape)
+    kt = "python3 " + os.path.join(ROOT, "bench.py") + (
+        f" --mode {args.kt_mode}" if args.kt_mode else "") + (
+        " --no-cpu-baseline" if args.no_cpu_baseline else "")
+    cmds = rocprof.plan(os.path.abspath(args.prof_dir), program,
+                        kt_program=kt if (args.kt_mode or not args.shape) else None)
+    if args.mode == "profile-plan":
+        print("\n".join(cmds))
+        return
+    # list only the passes this directory holds
+    cmds = [c for c in cmds if " -d " not in c or os.path.isdir(c.split(" -d ")[1].split()[0])]
+    timed = None
+    if args.bench_json:
+        line = [ln for ln in open(args.bench_json) if ln.strip().startswith("{")][-1]
+        b = json.loads(line)
+        if "warmup_steps_run" in b:
+            timed = (int(b["warmup_steps_run"]), int(b["steps"]))
+    summary = rocprof.collect(args.prof_dir, COPY_BYTES, timed=timed)
+    rel = [c.replace(ROOT, "$R") for c in cmds]
+    note = ("`R` is the repository root. "
+            f"Summary command: `python3 bench.py --mode summarize --prof-dir {args.prof_dir}"
+            + (f" --shape {args.shape}" if args.shape else "")
+            + (" --bench-json <the profiled bench's stdout>" if args.bench_json else "")
+            + (f" --kt-mode {args.kt_mode}" if args.kt_mode else "")
+            + "`. "
+            + ("The traffic program runs one 256 MiB device copy (the counter calibration) "
+               "and one step (attn_fwd, attn_bwd) of the workload. "
+               if any("--pmc" in c for c in cmds) else "")
+            + (f"The kernel trace profiles the default bench; its timed steps are dispatches "
+               f"{timed[0]}..{timed[0] + timed[1] - 1} of each per-step kernel." if timed else ""))
+    print(rocprof.render(summary, args.title, rel, note))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -348,14 +384,30 @@ def main():
     ap.add_argument("--shape", default=None,
                     help="traffic mode only: run the step on B,H,n,d (bf16, seed 1003) instead "
                          "of the default workload, e.g. 1,16,8192,128 for the d = 128 kernels")
-    ap.add_argument("--mode", choices=("bench", "traffic", "configs", "splitkv", "memory"), default="bench",
+    ap.add_argument("--prof-dir", default=None,
+                    help="profile-plan / summarize: directory of the rocprofv3 passes")
+    ap.add_argument("--bench-json", default=None,
+                    help="summarize: the JSON line the profiled default bench printed (selects "
+                         "the timed steps' dispatches in the kernel trace)")
+    ap.add_argument("--title", default="rocprofv3 summary", help="summarize: heading")
+    ap.add_argument("--kt-mode", default=None,
+                    help="profile-plan / summarize: bench mode the kernel-trace pass runs "
+                         "(default: the default bench; with --shape: the traffic program)")
+    ap.add_argument("--mode", choices=("bench", "traffic", "configs", "splitkv", "memory",
+                                       "profile-plan", "summarize"), default="bench",
                     help="traffic: one 256 MiB copy (counter calibration) and one step, "
                          "for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs; configs: time "
                          "the forward on all five workloads (and the backward where the "
                          "workload trains), one JSON line with a row per workload; splitkv: "
                          "unsplit vs split-key forward on small-grid and decoding shapes; memory: "
-                         "device-memory overhead per query row at n = 1024 .. 16384")
+                         "device-memory overhead per query row at n = 1024 .. 16384; "
+                         "profile-plan: print the rocprofv3 commands of every pass (kernel trace "
+                         "of the default bench, counter runs of --mode traffic) into --prof-dir; "
+                         "summarize: reduce those passes to the markdown kept under profiles/")
     args = ap.parse_args()
+    if args.mode in ("profile-plan", "summarize"):
+        profile_tools(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the attention "
               "kernels shard by (batch, head) with no communication, so per-GPU throughput "
@@ -458,16 +510,24 @@ def main():
     # launch duration is taken from HIP events around each attn_bwd call on the
     # launch stream; that call also runs the O(n*d) row pass (a few
     # microseconds), so the figure is a slight underestimate.
+    fig = recorded_figures(DOMINANT_KERNEL)
+    traffic = fig.get("hbm_bytes")
     roofline = {
-        "kernel": "bwd_main_kernel<64, 8>",
+        "kernel": DOMINANT_KERNEL,
         "bound": "mfma",
         "achieved": bwd_tf,
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": bwd_tf / PEAK_BF16_TFLOPS,
-        "traffic": recorded_traffic(),
+        "traffic": traffic,
         "avg_launch_ms": b_avg,
         "flops_per_launch": bwd_flops,
+        # from the committed counter summary of this kernel's current source (else null):
+        # MFMA pipe busy share of cycles (executed MFMA work, 14/10 of the algorithmic
+        # work in this design) and HBM GB/s = traffic / this run's launch time
+        "mfma_busy": fig.get("mfma_busy"),
+        "hbm_gbs": traffic / (b_avg * 1e-3) / 1e9 if traffic else None,
+        "counters_from": fig.get("profiles"),
     }
     out = {
         "metric": METRIC,
