@@ -332,9 +332,75 @@ def sweep_memory():
     return {"mode": "memory", "rows": rows}
 
 
-def _traffic_program(shape):
-    return "python3 " + os.path.join(ROOT, "bench.py") + " --mode traffic" + (
+def _traffic_program(shape, mode="traffic"):
+    return "python3 " + os.path.join(ROOT, "bench.py") + f" --mode {mode}" + (
         f" --shape {shape}" if shape else "")
+
+
+def run_probes():
+    """Runs the probe program as a child process and derives, per probe, the issue
+    cost of one instruction: cycles per instruction per wave and, with w waves on
+    each SIMD, SIMD cycles per instruction = cycles per iteration / (w x instructions
+    per iteration). VALU costs are also given relative to v_add_f32 at the same
+    wave count. The mixed probes put an MFMA body and an FMA body on one SIMD (two
+    waves, or interleaved in one wave); overlap = 1 - (time together) / (sum of the
+    times alone)."""
+    import subprocess
+    exe = os.path.join(ROOT, "memory_efficient_exact_amd", "probes", "mea_probe")
+    if not os.path.exists(exe):
+        sys.exit(f"{exe} is missing: build with `python -m memory_efficient_exact_amd.build`")
+    log("running the issue-cost probes ...")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    if r.returncode != 0:
+        sys.exit(f"probe program failed ({r.returncode}): {r.stderr[-2000:]}")
+    raw = json.loads(r.stdout.strip().splitlines()[-1])
+    out = {"mode": "probe", "raw": raw, "derived": {}}
+    alone = {}
+    for p in raw["probes"]:
+        name, w = p["probe"], p["waves_per_simd"]
+        if p["mfma_per_iter"] and not p["valu_per_iter"]:
+            cyc = p["mfma_wave_cycles_per_iter"]
+            alone[("mfma", w)] = cyc
+            out["derived"][f"{name} w{w}"] = {
+                "simd_cycles_per_mfma": cyc / (w * p["mfma_per_iter"]),
+                "flop_per_cycle_per_simd": 32 * 32 * 16 * 2 * w * p["mfma_per_iter"] / cyc,
+                "clock_mhz": p["clock_mhz"]}
+        elif p["valu_per_iter"] and not p["mfma_per_iter"]:
+            cyc = p["valu_wave_cycles_per_iter"]
+            alone[(name, w)] = cyc
+            out["derived"][f"{name} w{w}"] = {
+                "wave_cycles_per_instr": cyc / p["valu_per_iter"],
+                "simd_cycles_per_instr": cyc / (w * p["valu_per_iter"]), "clock_mhz": p["clock_mhz"]}
+    for key, d in out["derived"].items():
+        name, w = key.rsplit(" w", 1)
+        base = alone.get(("v_add_f32", int(w)))
+        if base and (name, int(w)) in alone:
+            d["cost_vs_v_add_f32"] = alone[(name, int(w))] / base
+    for p in raw["probes"]:
+        if not (p["mfma_per_iter"] and p["valu_per_iter"]):
+            continue
+        w = p["waves_per_simd"]
+        # the MFMA wave's time (in the two-wave probe the FMA wave runs alongside)
+        cyc = p["mfma_wave_cycles_per_iter"]
+        kind = "v_exp_f32" if "exp" in p["probe"] else "v_fma_f32"
+        valu_alone = alone.get((kind, 1), 0.0) * p["valu_per_iter"] / 8  # one wave, alone
+        mfma_alone = alone.get(("mfma", 1), 0.0)
+        per_simd_waves = 1 if p["probe"] == "mfma_wave+fma_wave" else w
+        d = {"cycles_per_iter": cyc, "mfma_per_iter_per_wave": p["mfma_per_iter"],
+             "valu_per_iter_per_wave": p["valu_per_iter"], "waves_per_simd": w,
+             # share of cycles the SIMD's matrix pipe is busy (32 cycles per MFMA)
+             "mfma_pipe_busy": 32.0 * p["mfma_per_iter"] * per_simd_waves / cyc,
+             "mfma_alone_cycles_per_iter": mfma_alone, "valu_alone_cycles_per_iter": valu_alone,
+             "clock_mhz": p["clock_mhz"]}
+        if p["probe"] == "mfma_wave+fma_wave":
+            d["fma_wave_cycles_per_iter"] = p["valu_wave_cycles_per_iter"]
+        if valu_alone and mfma_alone and per_simd_waves == 1:
+            # how much of the VALU work ran under the MFMAs (1: all of it)
+            d["valu_hidden"] = (mfma_alone + valu_alone - cyc) / valu_alone
+        out["derived"][p["probe"]] = d
+    out["derived"]["atomic_dq"] = {a["mode"]: {"tb_per_s": a["tb_per_s"], "ms": a["ms"]}
+                                   for a in raw["atomic_dq"]}
+    return out
 
 
 def profile_tools(args):
@@ -342,7 +408,7 @@ def profile_tools(args):
     from memory_efficient_exact_amd import rocprof
     if not args.prof_dir:
         sys.exit("--prof-dir is required")
-    program = _traffic_program(args.shape)
+    program = _traffic_program(args.shape, args.pmc_mode)
     kt = "python3 " + os.path.join(ROOT, "bench.py") + (
         f" --mode {args.kt_mode}" if args.kt_mode else "") + (
         " --no-cpu-baseline" if args.no_cpu_baseline else "")
@@ -366,13 +432,20 @@ def profile_tools(args):
             + (f" --shape {args.shape}" if args.shape else "")
             + (" --bench-json <the profiled bench's stdout>" if args.bench_json else "")
             + (f" --kt-mode {args.kt_mode}" if args.kt_mode else "")
+            + (f" --pmc-mode {args.pmc_mode}" if args.pmc_mode != "traffic" else "")
+            + (" --probe-json <the probe run's stdout>" if args.probe_json else "")
             + "`. "
             + ("The traffic program runs one 256 MiB device copy (the counter calibration) "
                "and one step (attn_fwd, attn_bwd) of the workload. "
-               if any("--pmc" in c for c in cmds) else "")
+               if any("--pmc" in c for c in cmds) and args.pmc_mode == "traffic" else "")
             + (f"The kernel trace profiles the default bench; its timed steps are dispatches "
                f"{timed[0]}..{timed[0] + timed[1] - 1} of each per-step kernel." if timed else ""))
-    print(rocprof.render(summary, args.title, rel, note))
+    text = rocprof.render(summary, args.title, rel, note)
+    if args.probe_json:
+        probe = json.loads([ln for ln in open(args.probe_json) if ln.strip().startswith("{")][-1])
+        head, sep, tail = text.partition("Machine-readable")
+        text = head + rocprof.render_probes(probe) + "\n" + sep + tail
+    print(text)
 
 
 def main():
@@ -390,11 +463,15 @@ def main():
                     help="summarize: the JSON line the profiled default bench printed (selects "
                          "the timed steps' dispatches in the kernel trace)")
     ap.add_argument("--title", default="rocprofv3 summary", help="summarize: heading")
+    ap.add_argument("--probe-json", default=None,
+                    help="summarize: the JSON line `--mode probe` printed, rendered as tables")
+    ap.add_argument("--pmc-mode", default="traffic",
+                    help="profile-plan / summarize: bench mode the counter passes run")
     ap.add_argument("--kt-mode", default=None,
                     help="profile-plan / summarize: bench mode the kernel-trace pass runs "
                          "(default: the default bench; with --shape: the traffic program)")
     ap.add_argument("--mode", choices=("bench", "traffic", "configs", "splitkv", "memory",
-                                       "profile-plan", "summarize"), default="bench",
+                                       "profile-plan", "summarize", "probe"), default="bench",
                     help="traffic: one 256 MiB copy (counter calibration) and one step, "
                          "for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs; configs: time "
                          "the forward on all five workloads (and the backward where the "
@@ -403,10 +480,15 @@ def main():
                          "device-memory overhead per query row at n = 1024 .. 16384; "
                          "profile-plan: print the rocprofv3 commands of every pass (kernel trace "
                          "of the default bench, counter runs of --mode traffic) into --prof-dir; "
-                         "summarize: reduce those passes to the markdown kept under profiles/")
+                         "summarize: reduce those passes to the markdown kept under profiles/; "
+                         "probe: run the issue-cost probes (probes/mea_probe) and derive per-"
+                         "instruction costs, MFMA/VALU overlap and fp32 atomic throughput")
     args = ap.parse_args()
     if args.mode in ("profile-plan", "summarize"):
         profile_tools(args)
+        return
+    if args.mode == "probe":
+        print(json.dumps(run_probes()), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the attention "

@@ -1,8 +1,11 @@
-"""Build libmea.so (the HIP kernels plus the C ABI) for gfx950, in-tree.
+"""Build libmea.so (the HIP kernels plus the C ABI) for gfx950, in-tree, and the
+issue-cost probe program.
 
 Usage: ``python -m memory_efficient_exact_amd.build [-v]``. Each source under
 ``csrc/`` is compiled to an object in ``_build/`` (in parallel), then linked
-into ``memory_efficient_exact_amd/libmea.so`` atomically. Always recompiles.
+into ``memory_efficient_exact_amd/libmea.so`` atomically; ``probes/mea_probe.hip``
+becomes the executable ``probes/mea_probe`` (run by ``bench.py --mode probe``).
+Always recompiles.
 """
 
 import concurrent.futures
@@ -14,6 +17,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(os.path.dirname(PKG), "_build")
 LIB = os.path.join(PKG, "libmea.so")
+PROBE_SRC = os.path.join(PKG, "probes", "mea_probe.hip")
+PROBE = os.path.join(PKG, "probes", "mea_probe")
 ARCH = os.environ.get("MEA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -52,13 +57,16 @@ def build(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
     objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+    probe_tmp = PROBE + ".tmp"
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
         futs = [ex.submit(_run, [HIPCC, *FLAGS, "-c", s, "-o", o], verbose) for s, o in zip(srcs, objs)]
+        futs.append(ex.submit(_run, [HIPCC, *FLAGS, PROBE_SRC, "-o", probe_tmp], verbose))
         for f in futs:
             f.result()
     tmp = LIB + ".tmp"
     _run([HIPCC, *FLAGS, "-shared", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
+    os.replace(probe_tmp, PROBE)
     return LIB
 
 

@@ -217,16 +217,23 @@ def calibration(cnt, copy_bytes):
     return fr, fw
 
 
+PROBES = os.path.join(HERE, "probes")
+
+
 def source_files(kernel):
-    """Library sources a kernel's code comes from: the .hip file that defines it and
-    the shared device header."""
+    """Sources a kernel's code comes from (paths relative to the package): the .hip
+    file that defines it, and the shared device header for the library's kernels;
+    the issue-cost probes are self-contained."""
     base = re.match(r"\w+", kernel).group(0)
     pat = re.compile(r"\b" + re.escape(base) + r"\s*\(")
-    found = []
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith(".hip") and pat.search(open(os.path.join(CSRC, f)).read()):
-            found.append(f)
-    return found + ["mea_device.h"] if found else []
+    for d, extra in ((CSRC, ["csrc/mea_device.h"]), (PROBES, [])):
+        if not os.path.isdir(d):
+            continue
+        found = [os.path.relpath(os.path.join(d, f), HERE) for f in sorted(os.listdir(d))
+                 if f.endswith(".hip") and pat.search(open(os.path.join(d, f)).read())]
+        if found:
+            return found + extra
+    return []
 
 
 def source_hash(kernel):
@@ -235,8 +242,8 @@ def source_hash(kernel):
         return None
     h = hashlib.sha256()
     for f in files:
-        h.update(f.encode())
-        h.update(open(os.path.join(CSRC, f), "rb").read())
+        h.update(os.path.basename(f).encode())
+        h.update(open(os.path.join(HERE, f), "rb").read())
     return h.hexdigest()
 
 
@@ -383,6 +390,33 @@ def render(summary, title, commands, note=""):
     out += ["Machine-readable (read by `bench.py`; `source_sha256` covers the files that define "
             "each kernel, so a changed kernel stops matching):", "", "```json",
             json.dumps(summary, indent=1, sort_keys=True), "```", ""]
+    return "\n".join(out)
+
+
+def render_probes(probe):
+    """Markdown tables of `bench.py --mode probe` output (issue costs, overlap,
+    LDS-fed MFMA rate, fp32 atomic throughput)."""
+    out = ["Issue-cost probes (`bench.py --mode probe`; per-wave core cycles from `s_memtime`, "
+           "the clock from `s_memtime` over `s_memrealtime`):", "",
+           "| probe | waves per SIMD | clock MHz | cycles per iteration (MFMA wave) | "
+           "cycles per iteration (VALU wave) | MFMAs per iteration | VALU instr. per iteration |",
+           "|---|---|---|---|---|---|---|"]
+    for p in probe["raw"]["probes"]:
+        out.append(f"| {p['probe']} | {p['waves_per_simd']} | {p['clock_mhz']:.0f} | "
+                   f"{p['mfma_wave_cycles_per_iter']:.1f} | {p['valu_wave_cycles_per_iter']:.1f} | "
+                   f"{p['mfma_per_iter']} | {p['valu_per_iter']} |")
+    out += ["", "Derived:", "", "| probe | figures |", "|---|---|"]
+    for k, v in probe["derived"].items():
+        if k == "atomic_dq":
+            continue
+        txt = ", ".join(f"{a} {b:.3f}" if isinstance(b, float) else f"{a} {b}" for a, b in v.items())
+        out.append(f"| {k} | {txt} |")
+    out += ["", "fp32 atomic adds in the single-pass backward's dQ pattern (1 x 16 x 16384 x 64, "
+            "256-key workgroups, 4.29 GB added; best of three):", "",
+            "| mode | ms | TB/s |", "|---|---|---|"]
+    for a in probe["raw"]["atomic_dq"]:
+        out.append(f"| {a['mode']} | {a['ms']:.3f} | {a['tb_per_s']:.2f} |")
+    out.append("")
     return "\n".join(out)
 
 
