@@ -83,7 +83,7 @@ def test_collect_and_derive(prof):
     assert e["hbm_read_bytes"] == pytest.approx(2 * 1024 * 1024)
     assert e["hbm_write_bytes"] == pytest.approx(512 * 1024)
     assert e["hbm_gbs"] == pytest.approx(2.5 * 2 ** 20 / 2.5e-3 / 1e9)
-    assert e["source_files"] == ["bwd_bf16.hip", "mea_device.h"]
+    assert e["source_files"] == ["csrc/bwd_bf16.hip", "csrc/mea_device.h"]
     assert e["source_sha256"] == rocprof.source_hash("bwd_main_kernel<64, 8>")
 
 
