@@ -524,7 +524,6 @@ __device__ __forceinline__ void dkdv_role128(const BwdArgs& a, int wg, bf16* s0,
   using TQ = SwzDma128<kTileQ, W>;
   constexpr int DK = D / 32;        // k-steps of the score products
   constexpr int DB = D / 16;        // 16-row blocks of dV^T, dK^T
-  constexpr int QB = kTileQ / 16;   // 16-row score blocks per tile
   constexpr int NC = kTileQ / 32;   // 32-row chunks (k-steps of dV, dK products)
 
   const int n_q = a.n_q, n_k = a.n_k;
