@@ -130,9 +130,12 @@ MEA_API size_t attn_bwd_workspace_bytes(mea_dtype_t dt, int64_t B, int64_t H, in
  * O(n^2) Memory": abstract; 方法详解; English digest method bullets). The
  * textbook Jacobian of the softmax is used:
  *   P = softmax(S), S = Q K^T / sqrt(d);  dV = P^T dO;  dP = dO V^T;
- *   D_i = sum_c dO_ic O_ic;  dS = P * (dP - D);  dQ = dS K / sqrt(d);
- *   dK = dS^T Q / sqrt(d).
+ *   D_i = sum_j P_ij dP_ij = sum_c dO_ic O_ic;  dS = P * (dP - D);
+ *   dQ = dS K / sqrt(d);  dK = dS^T Q / sqrt(d).
  * P is rebuilt tile by tile from row_max and row_sum; no n x n array exists.
+ * bf16 inputs take D from o (dO . O, fp32); fp32 inputs form it from the
+ * rebuilt P and dP (sum_j P_ij dP_ij / sum_j P_ij, in fp64), which keeps each
+ * row of dS summing to zero where one key dominates the row, and do not read o.
  *
  * q, k, v, o, dO : inputs [B,H,n,d] in dt (o from attn_fwd on the same q,k,v).
  * row_max, row_sum : the fp32 [B,H,n] statistics attn_fwd wrote for these
@@ -146,8 +149,8 @@ MEA_API size_t attn_bwd_workspace_bytes(mea_dtype_t dt, int64_t B, int64_t H, in
  *              (the row terms, or the whole split layout) must not overlap the
  *              inputs or outputs.
  * Supported: dt in {MEA_DTYPE_BF16, MEA_DTYPE_F32} with d in {64, 128}. fp32
- * inputs form scores on fp64 MFMA and the exponent in fp64, as the forward
- * does; everything else is fp32.
+ * inputs form scores and dP on fp64 MFMA and the exponent in fp64, as the
+ * forward does, and accumulate dQ, dK, dV on fp64 MFMA; P and dS are fp32.
  */
 MEA_API mea_status_t attn_bwd(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, int64_t d,
                       const void* q, const void* k, const void* v, const void* o,

@@ -5,7 +5,7 @@
 // keeps two numbers per query row, the probability tiles are rebuilt from
 // them ("Self-attention Does Not Need O(n^2) Memory": abstract; 方法详解;
 // English digest method bullets), and the gradients are the textbook softmax
-// Jacobian: dV = P^T dO, dP = dO V^T, D_i = dO_i . O_i, dS = P * (dP - D),
+// Jacobian: dV = P^T dO, dP = dO V^T, D_i = sum_j P_ij dP_ij, dS = P * (dP - D),
 // dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d).
 //
 // Precision (the 1e-5 bar of fp32 inputs). As in the fp32 forward, an fp32
