@@ -24,11 +24,13 @@
 // statistics; the fp32 forward reports l relative to its reported (rounded)
 // m, so the pair reproduces the row's log-sum-exp to fp32 rounding of l alone.
 //
-// Three launches on the caller's stream (the caller's O is not read):
-//  1. bwd_lse_f32: lse2 of every query row into the workspace (fp64).
-//  2. bwd_dterm_f32: -D of every query row (fp64), by a sweep over all keys of
-//     the row's head that forms S, dP and P as the main kernel does.
-//  3. bwd_main_f32: dK/dV workgroups (64 keys, 16 per wave, K and V of the
+// Launches on the caller's stream (the caller's O is not read):
+//  1. bwd_dterm_f32: the row terms {lse2, -D} (fp64), D by a sweep over all
+//     keys of the row's head that forms S, dP and P as the main kernel does.
+//     On a split grid (below) the sweep is cut into the dQ workgroups' key
+//     ranges; each range leaves its fp64 sums of P and P*dP, and
+//     bwd_dterm_merge_f32 adds them per row in range order.
+//  2. bwd_main_f32: dK/dV workgroups (64 keys, 16 per wave, K and V of the
 //     wave's keys in registers) sweeping 32-row query tiles of Q, dO and the
 //     row terms staged in LDS; then dQ workgroups (64 queries, Q and dO in
 //     registers) sweeping 32-key tiles of K, V. Every output element is
@@ -67,15 +69,11 @@ struct RowTerm {
 static_assert(sizeof(RowTerm) == 16, "row term layout");
 
 // ------------------------------------------------------------ 1. row terms
-// One thread per query row: lse2 = m*log2(e) + log2(l) in fp64 from the forward's
-// statistics. The D pass below completes each row's term.
-__global__ __launch_bounds__(kThreads) void bwd_lse_f32_kernel(const float* __restrict__ Mx,
-                                                               const float* __restrict__ Ls,
-                                                               RowTerm* __restrict__ terms,
-                                                               int64_t rows) {
-  for (int64_t row = (int64_t)blockIdx.x * kThreads + threadIdx.x; row < rows;
-       row += (int64_t)gridDim.x * kThreads)
-    terms[row].lse2 = (double)Mx[row] * 1.4426950408889634 + log2((double)Ls[row]);
+// lse2 = m*log2(e) + log2(l) in fp64 from the forward's statistics. The D pass
+// and the merge of its split ranges both form it with this one function, so
+// the two paths store the same value.
+__device__ __forceinline__ double row_lse2(float m, float l) {
+  return (double)m * 1.4426950408889634 + log2((double)l);
 }
 
 // ------------------------------------------------------------ 2. main kernel
@@ -376,34 +374,49 @@ __device__ __forceinline__ void dq_role32(const BwdArgs32& a, int wg, float* sK,
 // (about 9 at the x30 stress scale, where even a correctly rounded fp32 O
 // costs 7e-6). Grid and sweep as the dQ role: 64 query rows per workgroup
 // (lane = query), 32-key tiles of K and V staged in LDS.
+// fp64 sums of one key range's P and P*dP for one query row (split D pass)
+struct DPart {
+  double sum_p;
+  double sum_pdp;
+};
+static_assert(sizeof(DPart) == 16, "D partial layout");
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dterm_f32_kernel(const BwdArgs32 a,
-                                                                     RowTerm* __restrict__ terms) {
+                                                                     const float* __restrict__ Mx,
+                                                                     const float* __restrict__ Ls,
+                                                                     RowTerm* __restrict__ terms,
+                                                                     DPart* __restrict__ part) {
   constexpr int S = Shared32<D>::kStride;
   constexpr int KK = D / 4;
   __shared__ __attribute__((aligned(16))) float sK[Shared32<D>::kElems];
   __shared__ __attribute__((aligned(16))) float sV[Shared32<D>::kElems];
-  const int n_q = a.n_q, n_k = a.n_k;
+  const int n_q = a.n_q;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int tile = xcd_remap(blockIdx.x, (int)gridDim.x);  // bh * tiles_q + qt
-  const int bh = tile / a.tiles_q;
-  const int qt = tile - bh * a.tiles_q;
+  // ((bh * s_q) + sp) * tiles_q + qt: the dQ workgroups' ranges of key tiles
+  const int tile = xcd_remap(blockIdx.x, (int)gridDim.x);
+  const int bh = tile / (a.tiles_q * a.s_q);
+  const int sp = (tile - bh * a.tiles_q * a.s_q) / a.tiles_q;
+  const int qt = tile - (bh * a.s_q + sp) * a.tiles_q;
   const int64_t qbase = (int64_t)bh * n_q * D;
-  const float* Kh = a.K + (int64_t)bh * n_k * D;
-  const float* Vh = a.V + (int64_t)bh * n_k * D;
+  const int k_off = sp * a.len_k * kTile;
+  const int n_k = a.n_k - k_off;  // keys from the range's first on
+  const float* Kh = a.K + ((int64_t)bh * a.n_k + k_off) * D;
+  const float* Vh = a.V + ((int64_t)bh * a.n_k + k_off) * D;
   const int row = qt * kRows + wave * 16 + l16;  // this lane's query
   const int qrow = min(row, n_q - 1);
+  const int64_t trow = (int64_t)bh * n_q + qrow;
   float qf[KK], of[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     qf[kk] = a.Q[qbase + (int64_t)qrow * D + 4 * kk + g4];
     of[kk] = a.dO[qbase + (int64_t)qrow * D + 4 * kk + g4];
   }
-  const double lse2 = a.T[(int64_t)bh * n_q + qrow].lse2;
+  const double lse2 = row_lse2(Mx[trow], Ls[trow]);
   double sum_p = 0.0, sum_pdp = 0.0;
 
-  const int ntiles = (n_k + kTile - 1) / kTile;
+  const int ntiles = min(a.len_k, (n_k + kTile - 1) / kTile);  // tiles of this range
   Stage<D> stK, stV;
   stK.load(Kh, 0, n_k, tid);
   stV.load(Vh, 0, n_k, tid);
@@ -445,7 +458,26 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dterm_f32_kernel(const BwdArg
     sum_p += __shfl_xor(sum_p, off, 64);
     sum_pdp += __shfl_xor(sum_pdp, off, 64);
   }
-  if (row < n_q && g4 == 0) terms[(int64_t)bh * n_q + row].neg_d = -(sum_pdp / sum_p);
+  if (row < n_q && g4 == 0) {
+    if (a.s_q > 1) part[sp * a.q_rows + trow] = DPart{sum_p, sum_pdp};
+    else terms[trow] = RowTerm{lse2, -(sum_pdp / sum_p)};
+  }
+}
+
+// Split D pass: one thread per query row adds the ranges' sums in range order.
+__global__ __launch_bounds__(kThreads) void bwd_dterm_merge_f32_kernel(
+    const float* __restrict__ Mx, const float* __restrict__ Ls, const DPart* __restrict__ part,
+    int ranges, RowTerm* __restrict__ terms, int64_t rows) {
+  for (int64_t row = (int64_t)blockIdx.x * kThreads + threadIdx.x; row < rows;
+       row += (int64_t)gridDim.x * kThreads) {
+    double sum_p = 0.0, sum_pdp = 0.0;
+    for (int r = 0; r < ranges; ++r) {
+      const DPart d = part[r * rows + row];
+      sum_p += d.sum_p;
+      sum_pdp += d.sum_pdp;
+    }
+    terms[row] = RowTerm{row_lse2(Mx[row], Ls[row]), -(sum_pdp / sum_p)};
+  }
 }
 
 template <int D>
@@ -491,15 +523,19 @@ hipError_t launch(const BwdProblem& p, hipStream_t stream) {
   a.scale64 = 1.0 / sqrt((double)D);
   a.C64 = 1.4426950408889634 / sqrt((double)D);
   if (rows > 0) {
-    // row terms: lse2 per row, then D from the rows' own probabilities
-    hipLaunchKernelGGL(bwd_lse_f32_kernel, dim3(row_blocks(rows, kThreads)), dim3(kThreads), 0,
-                       stream, p.m, p.l, terms, rows);
+    // row terms; split: the D pass's range sums go where the dQ partials will
+    // later be written (16 bytes per row and range, against 4 * D)
+    DPart* part = q ? reinterpret_cast<DPart*>(p.part_dq) : nullptr;
+    hipLaunchKernelGGL((bwd_dterm_f32_kernel<D>), dim3((unsigned)a.total_q), dim3(kThreads), 0,
+                       stream, a, p.m, p.l, terms, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dterm_f32_kernel<D>), dim3((unsigned)(p.heads * a.tiles_q)),
-                       dim3(kThreads), 0, stream, a, terms);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (q) {
+      hipLaunchKernelGGL(bwd_dterm_merge_f32_kernel, dim3(row_blocks(rows, kThreads)),
+                         dim3(kThreads), 0, stream, p.m, p.l, part, a.s_q, terms, rows);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   hipLaunchKernelGGL((bwd_main_f32_kernel<D>), dim3((unsigned)(a.total_kv + a.total_q)),
                      dim3(kThreads), 0, stream, a);

@@ -107,7 +107,8 @@ struct BwdProblem {
   float* ws = nullptr;  // row terms: 8 (bf16) or 16 (fp32) bytes per query row
   BwdSplit split;
   // with split.kv > 1: [kv][heads * n_k][d] fp32 partials of dK and of dV;
-  // with split.q > 1: [q][heads * rows_q][d] fp32 partials of dQ (else null)
+  // with split.q > 1: [q][heads * rows_q][d] fp32 partials of dQ (else null);
+  // the fp32 backward's D pass first keeps its per-range sums there
   float* part_dk = nullptr;
   float* part_dv = nullptr;
   float* part_dq = nullptr;
