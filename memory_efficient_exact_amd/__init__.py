@@ -200,11 +200,15 @@ def _fwd_outputs(q, out, row_max, row_sum, stats):
 
 
 def _workspace(workspace, need, device):
+    """(workspace, its size in bytes): a contiguous tensor on `device`,
+    allocated with `need` bytes (at least 16) when the caller passes none."""
     import torch
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
+    if workspace.device != device:
+        raise ValueError(f"workspace is on {workspace.device}, expected {device}")
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -291,12 +295,7 @@ def attn_bwd(q, k, v, o, do, row_max, row_sum, dq=None, dk=None, dv=None, worksp
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         _check(name, t, q, di)
     B, H, n, d = q.shape
-    need = attn_bwd_workspace_bytes(dt, B, H, n, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if not workspace.is_cuda or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous GPU tensor")
-    wbytes = workspace.numel() * workspace.element_size()
+    workspace, wbytes = _workspace(workspace, attn_bwd_workspace_bytes(dt, B, H, n, d), q.device)
     dev = q.device
     st = _call(dev, lib().attn_bwd, dt, B, H, n, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
                _ptr(row_max), _ptr(row_sum), _ptr(dq), _ptr(dk), _ptr(dv),
