@@ -179,8 +179,8 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int wg, bf16* s0, bf
     dma.issue(a.dO + qbase, i0, n_q, odst);
     if (wave == W - 1) {
       const int r = min(i0 + lane, n_q - 1);
-      dma4(a.Lse2 + rbase + r, fdst);
-      dma4(a.Dv + rbase + r, fdst + kTileQ);
+      dma4_untracked(a.Lse2 + rbase + r, fdst);
+      dma4_untracked(a.Dv + rbase + r, fdst + kTileQ);
     }
   };
 

@@ -141,9 +141,39 @@ __device__ __forceinline__ void dma4(const void* gsrc, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (MEA_LDS void*)(lds_base), 4, 0, 0);
 }
 
+// The same two copies issued from inline assembly, out of sight of the
+// compiler's wait-count insertion. While that pass tracks a global->LDS copy
+// in flight it treats outstanding LDS reads as completing out of order, and
+// before using any one of them it waits for all (lgkmcnt(0)); without the
+// copy in view it waits only for the reads a use needs (lgkmcnt(n); LDS reads
+// return in issue order). The caller must wait for these copies itself before
+// the LDS they write is read or rewritten: wait_all() (vmcnt 0) and a barrier,
+// which the d = 64 backward does at the end of every staged tile. Waits the
+// compiler does place can only grow stricter, since the copies also count in
+// vmcnt. M0 holds the wave-uniform LDS address (one wait state after writing
+// it before the copy). The instruction writes no register, so nothing is left
+// in flight for the compiler to reuse.
+__device__ __forceinline__ void dma16_untracked(const void* gsrc, void* lds_base) {
+  const uint32_t lds =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MEA_LDS void*)(lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_untracked(const void* gsrc, void* lds_base) {
+  const uint32_t lds =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MEA_LDS void*)(lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(gsrc), "s"(lds)
+               : "memory", "m0");
+}
+
 // Copies a tile of ROWS consecutive rows of a row-major [*, D] bf16 array
-// into the padded LDS layout with 16-byte DMA, spread over the waves of a
-// workgroup. DMA block b covers LDS slots 64b..64b+63; slot s is row
+// into the padded LDS layout with 16-byte DMA (untracked, see above: the
+// d = 64 backward, its only user, measured 3-5% faster that way with identical
+// results), spread over the waves of a workgroup. DMA block b covers LDS slots 64b..64b+63; slot s is row
 // s / kSlotsPerRow, chunk s % kSlotsPerRow. Pad slots fetch a duplicate of
 // the row's first chunk. Source rows at or past `n` are clamped to n - 1,
 // so every global read stays inside the tensor.
@@ -177,7 +207,7 @@ struct TileDma {
       const int b = wave + WAVES * i;
       if (b < kBlocks) {
         const int sr = min(r0 + row[i], n - 1);
-        dma16(src + (int64_t)sr * D + col[i], dst + b * 512);
+        dma16_untracked(src + (int64_t)sr * D + col[i], dst + b * 512);
       }
     }
   }
