@@ -343,8 +343,9 @@ def run_probes():
     each SIMD, SIMD cycles per instruction = cycles per iteration / (w x instructions
     per iteration). VALU costs are also given relative to v_add_f32 at the same
     wave count. The mixed probes put an MFMA body and an FMA body on one SIMD (two
-    waves, or interleaved in one wave); overlap = 1 - (time together) / (sum of the
-    times alone)."""
+    waves, or interleaved in one wave): valu_hidden is the share of the VALU body's
+    own time that ran under the MFMAs. The exponential mixes alternate v_exp_f32 with
+    v_add_f32 or v_fma_f32: time_vs_serial_sum is 1 when they do not overlap."""
     import subprocess
     exe = os.path.join(ROOT, "memory_efficient_exact_amd", "probes", "mea_probe")
     if not os.path.exists(exe):
@@ -360,7 +361,8 @@ def run_probes():
         name, w = p["probe"], p["waves_per_simd"]
         if p["mfma_per_iter"] and not p["valu_per_iter"]:
             cyc = p["mfma_wave_cycles_per_iter"]
-            alone[("mfma", w)] = cyc
+            if name == "mfma_32x32x16_bf16":  # register operands only (not the LDS-fed probes)
+                alone[("mfma", w)] = cyc
             out["derived"][f"{name} w{w}"] = {
                 "simd_cycles_per_mfma": cyc / (w * p["mfma_per_iter"]),
                 "flop_per_cycle_per_simd": 32 * 32 * 16 * 2 * w * p["mfma_per_iter"] / cyc,
@@ -376,6 +378,12 @@ def run_probes():
         base = alone.get(("v_add_f32", int(w)))
         if base and (name, int(w)) in alone:
             d["cost_vs_v_add_f32"] = alone[(name, int(w))] / base
+        if "+" in name and (name, int(w)) in alone:
+            # two kinds alternating, four of each per iteration: the time against the
+            # sum of four of each alone (1: they serialise; 0.5: full overlap)
+            parts = [alone.get((k, int(w))) for k in name.split("+")]
+            if all(parts):
+                d["time_vs_serial_sum"] = alone[(name, int(w))] / sum(c / 2 for c in parts)
     for p in raw["probes"]:
         if not (p["mfma_per_iter"] and p["valu_per_iter"]):
             continue

@@ -23,7 +23,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kCUs = 256;
-constexpr int kIters = 2048;
+constexpr int kIters = 2048;  // a multiple of 4 (the register-only loops run four iterations per pass)
+static_assert(kIters % 4 == 0, "run_loop is unrolled by four");
 
 enum Kind : int {
   kMfma = 0,    // 4 independent v_mfma_f32_32x32x16_bf16 chains
@@ -44,6 +45,8 @@ enum Kind : int {
   kMfmaLdsTr,    // 4 MFMAs whose A operands come from 8 ds_read_b64_tr_b16 of LDS
   kMfmaLdsPre,   // as kMfmaLds, each iteration's operands read one iteration ahead
   kMfmaLdsTrPre, // as kMfmaLdsTr, read one iteration ahead
+  kExpAdd,       // 4 v_exp_f32 and 4 v_add_f32, alternating (does the exponential overlap?)
+  kExpFma,       // 4 v_exp_f32 and 4 v_fma_f32, alternating
   kKinds
 };
 const char* kNames[kKinds] = {"mfma_32x32x16_bf16", "v_fma_f32", "v_add_f32", "v_mul_f32",
@@ -52,10 +55,11 @@ const char* kNames[kKinds] = {"mfma_32x32x16_bf16", "v_fma_f32", "v_add_f32", "v
                               "one_wave:4mfma+32fma", "one_wave:4mfma+8exp", "two_waves:4mfma+8fma_each",
                               "mfma_fed_by_ds_read_b128", "mfma_fed_by_ds_read_b64_tr_b16",
                               "mfma_fed_by_ds_read_b128_read_ahead",
-                              "mfma_fed_by_ds_read_b64_tr_b16_read_ahead"};
+                              "mfma_fed_by_ds_read_b64_tr_b16_read_ahead",
+                              "v_exp_f32+v_add_f32", "v_exp_f32+v_fma_f32"};
 // MFMAs, and VALU instructions of the probed kind, per loop iteration
-constexpr int kMfmaPerIter[kKinds] = {4, 0, 0, 0, 0, 0, 0, 0, 4, 4, 4, 4, 4, 4, 4, 4, 4, 4};
-constexpr int kValuPerIter[kKinds] = {0, 8, 8, 8, 8, 8, 8, 8, 8, 8, 16, 32, 8, 8, 0, 0, 0, 0};
+constexpr int kMfmaPerIter[kKinds] = {4, 0, 0, 0, 0, 0, 0, 0, 4, 4, 4, 4, 4, 4, 4, 4, 4, 4, 0, 0};
+constexpr int kValuPerIter[kKinds] = {0, 8, 8, 8, 8, 8, 8, 8, 8, 8, 16, 32, 8, 8, 0, 0, 0, 0, 8, 8};
 // LDS probes: a 32 KiB tile of bf16 per workgroup; every read stays inside it
 constexpr int kLdsElems = 16384;
 
@@ -86,6 +90,26 @@ __device__ __forceinline__ void valu_body(float& x0, float& x1, float& x2, float
   if constexpr (K == kMax3) { VALU8("v_max3_f32 %0, %0, %1, %2") }
   if constexpr (K == kCvtPk) { VALU8("v_cvt_pk_bf16_f32 %0, %1, %2") }
   if constexpr (K == kPkFmaF16) { VALU8("v_pk_fma_f16 %0, %1, %2, %0") }
+  if constexpr (K == kExpAdd) {
+    asm volatile("v_exp_f32 %0, -%0" : "+v"(x0));
+    asm volatile("v_add_f32 %0, %1, %0" : "+v"(x1) : "v"(a));
+    asm volatile("v_exp_f32 %0, -%0" : "+v"(x2));
+    asm volatile("v_add_f32 %0, %1, %0" : "+v"(x3) : "v"(a));
+    asm volatile("v_exp_f32 %0, -%0" : "+v"(x4));
+    asm volatile("v_add_f32 %0, %1, %0" : "+v"(x5) : "v"(a));
+    asm volatile("v_exp_f32 %0, -%0" : "+v"(x6));
+    asm volatile("v_add_f32 %0, %1, %0" : "+v"(x7) : "v"(a));
+  }
+  if constexpr (K == kExpFma) {
+    asm volatile("v_exp_f32 %0, -%0" : "+v"(x0));
+    asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(x1) : "v"(a), "v"(b));
+    asm volatile("v_exp_f32 %0, -%0" : "+v"(x2));
+    asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(x3) : "v"(a), "v"(b));
+    asm volatile("v_exp_f32 %0, -%0" : "+v"(x4));
+    asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(x5) : "v"(a), "v"(b));
+    asm volatile("v_exp_f32 %0, -%0" : "+v"(x6));
+    asm volatile("v_fma_f32 %0, %1, %2, %0" : "+v"(x7) : "v"(a), "v"(b));
+  }
 }
 
 struct Mfma4 {
@@ -104,13 +128,19 @@ struct Mfma4 {
   }
 };
 
-// one loop per wave; MFMA: 4 MFMAs per iteration; V: the VALU kind, N8 groups of 8
+// one loop per wave; MFMA: 4 MFMAs per iteration; V: the VALU kind, N8 groups of 8.
+// Unrolled by four (iters, kIters below, is a multiple of four): each scalar loop-control
+// instruction costs the wave issue cycles of its own, and three of them per
+// eight VALU instructions made v_add_f32 read 7.5 cycles per issue instead of ~5.
 template <bool MFMA, int V, int N8>
 __device__ __forceinline__ void run_loop(Mfma4& m, float* x, float a, float b, int iters) {
-  for (int it = 0; it < iters; ++it) {
-    if constexpr (MFMA) m.step();
+  for (int it = 0; it < iters; it += 4) {
 #pragma unroll
-    for (int g = 0; g < N8; ++g) valu_body<V>(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7], a, b);
+    for (int u = 0; u < 4; ++u) {
+      if constexpr (MFMA) m.step();
+#pragma unroll
+      for (int g = 0; g < N8; ++g) valu_body<V>(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7], a, b);
+    }
   }
 }
 
@@ -216,6 +246,7 @@ __global__ __launch_bounds__(512) void probe_kernel(WaveTime* out, float* sink, 
   else if constexpr (K == kMfmaLdsTr) lds_loop<true, false>(m, lds, lane, iters);
   else if constexpr (K == kMfmaLdsPre) lds_loop<false, true>(m, lds, lane, iters);
   else if constexpr (K == kMfmaLdsTrPre) lds_loop<true, true>(m, lds, lane, iters);
+  else if constexpr (K == kExpAdd || K == kExpFma) run_loop<false, K, 1>(m, x, a, b, iters);
   const unsigned long long t1 = __builtin_amdgcn_s_memtime();
   const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
   if (lane == 0) out[gw] = WaveTime{t1 - t0, r1 - r0, role, 0};
@@ -270,7 +301,7 @@ void launch_probe(int kind, dim3 grid, dim3 block, WaveTime* out, float* sink, i
 #define CASE(K) case K: hipLaunchKernelGGL(probe_kernel<K>, grid, block, 0, 0, out, sink, iters, 0); break;
     CASE(kMfma) CASE(kFma) CASE(kAdd) CASE(kMul) CASE(kExp) CASE(kMax3) CASE(kCvtPk) CASE(kPkFmaF16)
     CASE(kMixTwoWaves) CASE(kMix1Fma8) CASE(kMix1Fma16) CASE(kMix1Fma32) CASE(kMix1Exp8) CASE(kMix2Fma8)
-    CASE(kMfmaLds) CASE(kMfmaLdsTr) CASE(kMfmaLdsPre) CASE(kMfmaLdsTrPre)
+    CASE(kMfmaLds) CASE(kMfmaLdsTr) CASE(kMfmaLdsPre) CASE(kMfmaLdsTrPre) CASE(kExpAdd) CASE(kExpFma)
 #undef CASE
   }
 }
@@ -304,6 +335,8 @@ int main() {
   runs.push_back({kMix2Fma8, 2});
   for (int k = kMfmaLds; k <= kMfmaLdsTrPre; ++k)
     for (int w : {1, 2}) runs.push_back({k, w});
+  for (int k = kExpAdd; k <= kExpFma; ++k)
+    for (int w : {1, 2, 4}) runs.push_back({k, w});
   for (const Run& r : runs) {
     // 4-wave blocks, one wave per SIMD, w blocks per CU; the two-wave probe uses
     // 8-wave blocks (one MFMA wave and one FMA wave per SIMD)
