@@ -354,7 +354,11 @@ def run_probes():
     r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
     if r.returncode != 0:
         sys.exit(f"probe program failed ({r.returncode}): {r.stderr[-2000:]}")
-    raw = json.loads(r.stdout.strip().splitlines()[-1])
+    return derive_probes(json.loads(r.stdout.strip().splitlines()[-1]))
+
+
+def derive_probes(raw):
+    """The derived figures of run_probes from the probe program's JSON."""
     out = {"mode": "probe", "raw": raw, "derived": {}}
     alone = {}
     for p in raw["probes"]:

@@ -121,3 +121,36 @@ def test_mangled_library_names():
         == "bwd_reduce_kernel<128, __bf16>"
     assert rocprof.short_name("_ZN3mea12_GLOBAL__N_115fwd_bf16_kernelILi64ELi1ELi128ELb1ELi4EEEvNS0_7FwdArgsE") \
         == "fwd_bf16_kernel<64, 1, 128, true, 4>"
+
+
+# ------------------------------------------------------------ probe derivation
+
+def _probe(name, w, mfma_cyc, valu_cyc, mfma, valu):
+    return {"probe": name, "waves_per_simd": w, "clock_mhz": 2000.0,
+            "mfma_wave_cycles_per_iter": mfma_cyc, "valu_wave_cycles_per_iter": valu_cyc,
+            "mfma_per_iter": mfma, "valu_per_iter": valu}
+
+
+def test_probe_derivation_uses_the_register_only_mfma_time():
+    import bench
+    raw = {"probes": [
+        _probe("mfma_32x32x16_bf16", 1, 128.0, 0.0, 4, 0),
+        # an LDS-fed MFMA probe after it must not replace the MFMA-alone time
+        _probe("mfma_fed_by_ds_read_b128", 1, 240.0, 0.0, 4, 0),
+        _probe("v_fma_f32", 1, 0.0, 44.0, 0, 8),
+        _probe("v_add_f32", 1, 0.0, 40.0, 0, 8),
+        _probe("v_exp_f32", 1, 0.0, 72.0, 0, 8),
+        _probe("v_exp_f32+v_add_f32", 1, 0.0, 56.0, 0, 8),
+        _probe("one_wave:4mfma+8fma", 1, 135.0, 0.0, 4, 8),
+    ], "atomic_dq": [{"mode": "atomic_add_f32", "ms": 4.0, "tb_per_s": 1.07}]}
+    d = bench.derive_probes(raw)["derived"]
+    assert d["mfma_32x32x16_bf16 w1"]["simd_cycles_per_mfma"] == 32.0
+    assert d["v_fma_f32 w1"]["wave_cycles_per_instr"] == 5.5
+    assert d["v_fma_f32 w1"]["cost_vs_v_add_f32"] == 1.1
+    # four exponentials (36 cycles) and four adds (20) alone: 56, so no overlap
+    assert abs(d["v_exp_f32+v_add_f32 w1"]["time_vs_serial_sum"] - 1.0) < 1e-12
+    mix = d["one_wave:4mfma+8fma"]
+    assert mix["mfma_alone_cycles_per_iter"] == 128.0
+    # 128 + 44 - 135 = 37 of the FMAs' 44 cycles ran under the MFMAs
+    assert abs(mix["valu_hidden"] - 37.0 / 44.0) < 1e-12
+    assert abs(mix["mfma_pipe_busy"] - 128.0 / 135.0) < 1e-12
