@@ -397,15 +397,21 @@ def derive_probes(raw):
         kind = "v_exp_f32" if "exp" in p["probe"] else "v_fma_f32"
         valu_alone = alone.get((kind, 1), 0.0) * p["valu_per_iter"] / 8  # one wave, alone
         mfma_alone = alone.get(("mfma", 1), 0.0)
-        per_simd_waves = 1 if p["probe"] == "mfma_wave+fma_wave" else w
+        two_waves = p["probe"] in ("mfma_wave+fma_wave", "mfma_wave+exp_wave")
+        per_simd_waves = 1 if two_waves else w
         d = {"cycles_per_iter": cyc, "mfma_per_iter_per_wave": p["mfma_per_iter"],
              "valu_per_iter_per_wave": p["valu_per_iter"], "waves_per_simd": w,
              # share of cycles the SIMD's matrix pipe is busy (32 cycles per MFMA)
              "mfma_pipe_busy": 32.0 * p["mfma_per_iter"] * per_simd_waves / cyc,
              "mfma_alone_cycles_per_iter": mfma_alone, "valu_alone_cycles_per_iter": valu_alone,
              "clock_mhz": p["clock_mhz"]}
-        if p["probe"] == "mfma_wave+fma_wave":
-            d["fma_wave_cycles_per_iter"] = p["valu_wave_cycles_per_iter"]
+        if two_waves:
+            # the VALU wave's own time beside the MFMA wave, against its time alone
+            d["valu_wave_cycles_per_iter"] = p["valu_wave_cycles_per_iter"]
+            if valu_alone:
+                d["valu_wave_slowdown"] = p["valu_wave_cycles_per_iter"] / valu_alone
+            if mfma_alone:
+                d["mfma_wave_slowdown"] = cyc / mfma_alone
         if valu_alone and mfma_alone and per_simd_waves == 1:
             # how much of the VALU work ran under the MFMAs (1: all of it)
             d["valu_hidden"] = (mfma_alone + valu_alone - cyc) / valu_alone

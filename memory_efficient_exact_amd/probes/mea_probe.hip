@@ -47,6 +47,7 @@ enum Kind : int {
   kMfmaLdsTrPre, // as kMfmaLdsTr, read one iteration ahead
   kExpAdd,       // 4 v_exp_f32 and 4 v_add_f32, alternating (does the exponential overlap?)
   kExpFma,       // 4 v_exp_f32 and 4 v_fma_f32, alternating
+  kMixTwoWavesExp,  // per SIMD: one wave runs the MFMA loop, another the v_exp_f32 loop
   kKinds
 };
 const char* kNames[kKinds] = {"mfma_32x32x16_bf16", "v_fma_f32", "v_add_f32", "v_mul_f32",
@@ -56,10 +57,10 @@ const char* kNames[kKinds] = {"mfma_32x32x16_bf16", "v_fma_f32", "v_add_f32", "v
                               "mfma_fed_by_ds_read_b128", "mfma_fed_by_ds_read_b64_tr_b16",
                               "mfma_fed_by_ds_read_b128_read_ahead",
                               "mfma_fed_by_ds_read_b64_tr_b16_read_ahead",
-                              "v_exp_f32+v_add_f32", "v_exp_f32+v_fma_f32"};
+                              "v_exp_f32+v_add_f32", "v_exp_f32+v_fma_f32", "mfma_wave+exp_wave"};
 // MFMAs, and VALU instructions of the probed kind, per loop iteration
-constexpr int kMfmaPerIter[kKinds] = {4, 0, 0, 0, 0, 0, 0, 0, 4, 4, 4, 4, 4, 4, 4, 4, 4, 4, 0, 0};
-constexpr int kValuPerIter[kKinds] = {0, 8, 8, 8, 8, 8, 8, 8, 8, 8, 16, 32, 8, 8, 0, 0, 0, 0, 8, 8};
+constexpr int kMfmaPerIter[kKinds] = {4, 0, 0, 0, 0, 0, 0, 0, 4, 4, 4, 4, 4, 4, 4, 4, 4, 4, 0, 0, 4};
+constexpr int kValuPerIter[kKinds] = {0, 8, 8, 8, 8, 8, 8, 8, 8, 8, 16, 32, 8, 8, 0, 0, 0, 0, 8, 8, 8};
 // LDS probes: a 32 KiB tile of bf16 per workgroup; every read stays inside it
 constexpr int kLdsElems = 16384;
 
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(512) void probe_kernel(WaveTime* out, float* sink, 
   }
   // in the two-wave probe the first four waves of a block (one per SIMD) run the
   // MFMA loop and the other four the FMA loop
-  const int role = (K == kMixTwoWaves && wave >= 4) || (kMfmaPerIter[K] == 0) ? 1 : 0;
+  const int role = ((K == kMixTwoWaves || K == kMixTwoWavesExp) && wave >= 4) || (kMfmaPerIter[K] == 0) ? 1 : 0;
   if constexpr (K >= kMfmaLds) {
     for (int i = threadIdx.x; i < kLdsElems; i += blockDim.x) lds[i] = (__bf16)(0.001f * (float)(i & 255));
   }
@@ -247,6 +248,10 @@ __global__ __launch_bounds__(512) void probe_kernel(WaveTime* out, float* sink, 
   else if constexpr (K == kMfmaLdsPre) lds_loop<false, true>(m, lds, lane, iters);
   else if constexpr (K == kMfmaLdsTrPre) lds_loop<true, true>(m, lds, lane, iters);
   else if constexpr (K == kExpAdd || K == kExpFma) run_loop<false, K, 1>(m, x, a, b, iters);
+  else if constexpr (K == kMixTwoWavesExp) {
+    if (role == 0) run_loop<true, kFma, 0>(m, x, a, b, iters);
+    else run_loop<false, kExp, 1>(m, x, a, b, iters);
+  }
   const unsigned long long t1 = __builtin_amdgcn_s_memtime();
   const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
   if (lane == 0) out[gw] = WaveTime{t1 - t0, r1 - r0, role, 0};
@@ -301,7 +306,7 @@ void launch_probe(int kind, dim3 grid, dim3 block, WaveTime* out, float* sink, i
 #define CASE(K) case K: hipLaunchKernelGGL(probe_kernel<K>, grid, block, 0, 0, out, sink, iters, 0); break;
     CASE(kMfma) CASE(kFma) CASE(kAdd) CASE(kMul) CASE(kExp) CASE(kMax3) CASE(kCvtPk) CASE(kPkFmaF16)
     CASE(kMixTwoWaves) CASE(kMix1Fma8) CASE(kMix1Fma16) CASE(kMix1Fma32) CASE(kMix1Exp8) CASE(kMix2Fma8)
-    CASE(kMfmaLds) CASE(kMfmaLdsTr) CASE(kMfmaLdsPre) CASE(kMfmaLdsTrPre) CASE(kExpAdd) CASE(kExpFma)
+    CASE(kMfmaLds) CASE(kMfmaLdsTr) CASE(kMfmaLdsPre) CASE(kMfmaLdsTrPre) CASE(kExpAdd) CASE(kExpFma) CASE(kMixTwoWavesExp)
 #undef CASE
   }
 }
@@ -331,6 +336,7 @@ int main() {
     for (int w : {1, 2, 4})
       if (k != kMfma || w < 4) runs.push_back({k, w});
   runs.push_back({kMixTwoWaves, 2});
+  runs.push_back({kMixTwoWavesExp, 2});
   for (int k = kMix1Fma8; k <= kMix1Exp8; ++k) runs.push_back({k, 1});
   runs.push_back({kMix2Fma8, 2});
   for (int k = kMfmaLds; k <= kMfmaLdsTrPre; ++k)
@@ -340,8 +346,9 @@ int main() {
   for (const Run& r : runs) {
     // 4-wave blocks, one wave per SIMD, w blocks per CU; the two-wave probe uses
     // 8-wave blocks (one MFMA wave and one FMA wave per SIMD)
-    const int wpb = r.kind == kMixTwoWaves ? 8 : 4;
-    const int blocks = r.kind == kMixTwoWaves ? kCUs : kCUs * r.waves_per_simd;
+    const bool two = r.kind == kMixTwoWaves || r.kind == kMixTwoWavesExp;
+    const int wpb = two ? 8 : 4;
+    const int blocks = two ? kCUs : kCUs * r.waves_per_simd;
     const int waves = blocks * wpb;
     if (waves > max_waves) return 3;
     for (int rep = 0; rep < 2; ++rep) {  // the first launch warms the clock

@@ -142,6 +142,7 @@ def test_probe_derivation_uses_the_register_only_mfma_time():
         _probe("v_exp_f32", 1, 0.0, 72.0, 0, 8),
         _probe("v_exp_f32+v_add_f32", 1, 0.0, 56.0, 0, 8),
         _probe("one_wave:4mfma+8fma", 1, 135.0, 0.0, 4, 8),
+        _probe("mfma_wave+exp_wave", 2, 160.0, 108.0, 4, 8),
     ], "atomic_dq": [{"mode": "atomic_add_f32", "ms": 4.0, "tb_per_s": 1.07}]}
     d = bench.derive_probes(raw)["derived"]
     assert d["mfma_32x32x16_bf16 w1"]["simd_cycles_per_mfma"] == 32.0
@@ -154,3 +155,8 @@ def test_probe_derivation_uses_the_register_only_mfma_time():
     # 128 + 44 - 135 = 37 of the FMAs' 44 cycles ran under the MFMAs
     assert abs(mix["valu_hidden"] - 37.0 / 44.0) < 1e-12
     assert abs(mix["mfma_pipe_busy"] - 128.0 / 135.0) < 1e-12
+    # an MFMA wave beside an exponential wave: each against its own time alone
+    two = d["mfma_wave+exp_wave"]
+    assert two["mfma_wave_slowdown"] == 160.0 / 128.0
+    assert two["valu_wave_slowdown"] == 108.0 / 72.0
+    assert abs(two["mfma_pipe_busy"] - 128.0 / 160.0) < 1e-12
