@@ -438,12 +438,23 @@ def profile_tools(args):
     # list only the passes this directory holds
     cmds = [c for c in cmds if " -d " not in c or os.path.isdir(c.split(" -d ")[1].split()[0])]
     timed = None
+    b = {}
     if args.bench_json:
         line = [ln for ln in open(args.bench_json) if ln.strip().startswith("{")][-1]
         b = json.loads(line)
         if "warmup_steps_run" in b:
             timed = (int(b["warmup_steps_run"]), int(b["steps"]))
     summary = rocprof.collect(args.prof_dir, COPY_BYTES, timed=timed)
+    agree = ""
+    if timed and "fwd" in b and "bwd" in b:
+        # the bench's HIP-event time per call against the trace's kernels of that call
+        ks = summary.get("kernels", {})
+        f_tr = sum(v.get("timed_avg_us") or 0.0 for k, v in ks.items() if k.startswith("fwd_")) / 1e3
+        b_tr = sum(v.get("timed_avg_us") or 0.0 for k, v in ks.items() if k.startswith("bwd_")) / 1e3
+        agree = (f" The profiled bench printed {b['fwd']['ms']:.4f} ms per forward and "
+                 f"{b['bwd']['ms']:.4f} ms per backward call (HIP events on the launch stream); "
+                 f"the trace's timed steps give {f_tr:.4f} ms and {b_tr:.4f} ms (each call's "
+                 f"kernels summed).")
     rel = [c.replace(ROOT, "$R") for c in cmds]
     note = ("`R` is the repository root. "
             f"Summary command: `python3 bench.py --mode summarize --prof-dir {args.prof_dir}"
@@ -457,7 +468,8 @@ def profile_tools(args):
                "and one step (attn_fwd, attn_bwd) of the workload. "
                if any("--pmc" in c for c in cmds) and args.pmc_mode == "traffic" else "")
             + (f"The kernel trace profiles the default bench; its timed steps are dispatches "
-               f"{timed[0]}..{timed[0] + timed[1] - 1} of each per-step kernel." if timed else ""))
+               f"{timed[0]}..{timed[0] + timed[1] - 1} of each per-step kernel." if timed else "")
+            + agree)
     text = rocprof.render(summary, args.title, rel, note)
     if args.probe_json:
         probe = json.loads([ln for ln in open(args.probe_json) if ln.strip().startswith("{")][-1])
