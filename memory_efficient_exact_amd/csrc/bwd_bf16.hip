@@ -478,7 +478,10 @@ struct Layout128 {
   }
 };
 
-template <int ROWS, int WAVES>
+// U: copies issued out of sight of the compiler's wait-count pass (dma16_untracked),
+// used by the d = 128 dQ role (1.2-1.6% faster, identical results; the dK/dV role
+// spills with them)
+template <int ROWS, int WAVES, bool U = false>
 struct SwzDma128 {
   using L = Layout128;
   static constexpr int kBlocks = ROWS * L::kChunks / 64;
@@ -506,7 +509,8 @@ struct SwzDma128 {
       const int b = wave + WAVES * i;
       if (b < kBlocks) {
         const int sr = min(r0 + row[i], n - 1);
-        dma16(src + (int64_t)sr * 128 + col[i], dst + b * 512);
+        if constexpr (U) dma16_untracked(src + (int64_t)sr * 128 + col[i], dst + b * 512);
+        else dma16(src + (int64_t)sr * 128 + col[i], dst + b * 512);
       }
     }
   }
@@ -670,7 +674,7 @@ __device__ __forceinline__ void dq_role128(const BwdArgs& a, int wg, bf16* s0, b
                                            bf16* s3) {
   constexpr int D = 128;
   using L = Layout128;
-  using TK = SwzDma128<kTileK, W>;
+  using TK = SwzDma128<kTileK, W, true>;
   constexpr int DK = D / 32;
   constexpr int DB = D / 16;
   constexpr int NC = kTileK / 32;  // 32-key chunks (k-steps of the dQ product)

@@ -91,3 +91,12 @@ def test_d64_backward_keeps_partial_lds_waits(tmp_path):
     full, partial = lds_waits(function_body(asm, r"_ZN3mea12_GLOBAL__N_115bwd_main_kernelILi64ELi8EEEv\w*"))
     # with the builtin copy all 666 were full; the untracked copies leave ~100+ partial
     assert partial >= 50 and partial > full, (full, partial)
+
+
+def test_d128_backward_dq_role_keeps_partial_lds_waits(tmp_path):
+    # the d = 128 kernel issues only its dQ role's tile copies out of the pass's sight
+    src = os.path.join(ROOT, "memory_efficient_exact_amd", "csrc", "bwd_bf16.hip")
+    asm = assemble(src, str(tmp_path / "bwd.s"))
+    full, partial = lds_waits(function_body(asm, r"_ZN3mea12_GLOBAL__N_118bwd_main128_kernelILi8EEEv\w*"))
+    # all 221 were full with the builtin copies in both roles
+    assert partial >= 40, (full, partial)
