@@ -151,23 +151,29 @@ __device__ __forceinline__ void dma4(const void* gsrc, void* lds_base) {
 // which the d = 64 backward does at the end of every staged tile. Waits the
 // compiler does place can only grow stricter, since the copies also count in
 // vmcnt. M0 holds the wave-uniform LDS address (one wait state after writing
-// it before the copy). The instruction writes no register, so nothing is left
-// in flight for the compiler to reuse.
+// it before the copy; the copy reads it at issue). M0 is a reserved register
+// whose clobber the compiler need not honour, so the asm saves it and puts it
+// back after the copy. The instruction writes no vector register, so nothing
+// is left in flight for the compiler to reuse.
 __device__ __forceinline__ void dma16_untracked(const void* gsrc, void* lds_base) {
   const uint32_t lds =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MEA_LDS void*)(lds_base));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+               "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
                : "v"(gsrc), "s"(lds)
-               : "memory", "m0");
+               : "memory");
 }
 __device__ __forceinline__ void dma4_untracked(const void* gsrc, void* lds_base) {
   const uint32_t lds =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(MEA_LDS void*)(lds_base));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+               "global_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
                : "v"(gsrc), "s"(lds)
-               : "memory", "m0");
+               : "memory");
 }
 
 // Copies a tile of ROWS consecutive rows of a row-major [*, D] bf16 array
