@@ -337,6 +337,65 @@ def _traffic_program(shape, mode="traffic"):
         f" --shape {shape}" if shape else "")
 
 
+SYNC_FWD_LAYOUTS = ("fwd row-tiled", "fwd decoding")
+SYNC_BWD_ROLES = ("bwd d=64 dK/dV", "bwd d=64 dQ", "bwd d=128 dK/dV", "bwd d=128 dQ")
+
+
+def derive_sync(fwd_counts, bwd_counts):
+    """Per tiled loop: {copy wait, barrier, loop cycles, tiles, waves} (sums over
+    waves, core cycles) -> cycles per tile and shares of the loop."""
+    out = {}
+    for names, counts in ((SYNC_FWD_LAYOUTS, fwd_counts), (SYNC_BWD_ROLES, bwd_counts)):
+        for i, name in enumerate(names):
+            wait, bar, loop, tiles, waves = counts[5 * i:5 * i + 5]
+            if tiles == 0 or loop == 0:
+                continue
+            out[name] = {
+                "waves": waves, "tiles_per_wave": tiles / waves,
+                "loop_cycles_per_tile": loop / tiles,
+                "copy_wait_cycles_per_tile": wait / tiles,
+                "barrier_cycles_per_tile": bar / tiles,
+                "copy_wait_share": wait / loop, "barrier_share": bar / loop,
+            }
+    return out
+
+
+def run_sync(step, outputs, calls, dev):
+    """Run `calls` steps through the timing library and return its end-of-tile
+    counters, derived, and whether its outputs equal libmea.so's bit for bit."""
+    import ctypes
+
+    import torch
+
+    import memory_efficient_exact_amd as mea
+    step()  # libmea.so
+    torch.cuda.synchronize(dev)
+    ref = [x.clone() for x in outputs]
+    T = mea.load(mea.timing_library_path())
+    u64 = ctypes.c_ulonglong
+    for fn in ("mea_sync_timers_fwd", "mea_sync_timers_bwd"):
+        getattr(T, fn).argtypes = [ctypes.POINTER(u64), ctypes.c_int]
+        getattr(T, fn).restype = ctypes.c_int
+    fwd, bwd = (u64 * 10)(), (u64 * 20)()
+    with mea.using(T):
+        t_warm = time.perf_counter()
+        while time.perf_counter() - t_warm < MIN_BENCH_WARM_S:
+            step()
+            torch.cuda.synchronize(dev)
+        if T.mea_sync_timers_fwd(fwd, 1) or T.mea_sync_timers_bwd(bwd, 1):
+            raise RuntimeError("reading the synchronisation counters failed")
+        t0 = time.perf_counter()
+        for _ in range(calls):
+            step()
+        torch.cuda.synchronize(dev)
+        wall_ms = (time.perf_counter() - t0) * 1e3 / calls
+        if T.mea_sync_timers_fwd(fwd, 1) or T.mea_sync_timers_bwd(bwd, 1):
+            raise RuntimeError("reading the synchronisation counters failed")
+    same = all(torch.equal(a, b) for a, b in zip(outputs, ref))
+    return {"mode": "sync", "steps": calls, "ms_per_step_wall": wall_ms,
+            "bitwise_equal_to_libmea": same, "loops": derive_sync(list(fwd), list(bwd))}
+
+
 def run_probes():
     """Runs the probe program as a child process and derives, per probe, the issue
     cost of one instruction: cycles per instruction per wave and, with w waves on
@@ -485,8 +544,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shape", default=None,
-                    help="traffic mode only: run the step on B,H,n,d (bf16, seed 1003) instead "
-                         "of the default workload, e.g. 1,16,8192,128 for the d = 128 kernels")
+                    help="traffic and sync modes: run the step on B,H,n,d (bf16, seed 1003) "
+                         "instead of the default workload, e.g. 1,16,8192,128 for the d = 128 "
+                         "kernels")
     ap.add_argument("--prof-dir", default=None,
                     help="profile-plan / summarize: directory of the rocprofv3 passes")
     ap.add_argument("--bench-json", default=None,
@@ -501,7 +561,8 @@ def main():
                     help="profile-plan / summarize: bench mode the kernel-trace pass runs "
                          "(default: the default bench; with --shape: the traffic program)")
     ap.add_argument("--mode", choices=("bench", "traffic", "configs", "splitkv", "memory",
-                                       "profile-plan", "summarize", "probe"), default="bench",
+                                       "profile-plan", "summarize", "probe", "sync"),
+                    default="bench",
                     help="traffic: one 256 MiB copy (counter calibration) and one step, "
                          "for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs; configs: time "
                          "the forward on all five workloads (and the backward where the "
@@ -512,7 +573,10 @@ def main():
                          "of the default bench, counter runs of --mode traffic) into --prof-dir; "
                          "summarize: reduce those passes to the markdown kept under profiles/; "
                          "probe: run the issue-cost probes (probes/mea_probe) and derive per-"
-                         "instruction costs, MFMA/VALU overlap and fp32 atomic throughput")
+                         "instruction costs, MFMA/VALU overlap and fp32 atomic throughput; sync: "
+                         "--steps steps through the timing library (libmea_synctimers.so): core "
+                         "cycles per staged tile spent waiting for the tile copies and at the "
+                         "barrier, per tiled loop, and a bitwise check against libmea.so")
     args = ap.parse_args()
     if args.mode in ("profile-plan", "summarize"):
         profile_tools(args)
@@ -544,8 +608,8 @@ def main():
         return
     w = inputgen.WORKLOADS["c3_long_bf16"]
     if args.shape is not None:
-        if args.mode != "traffic":
-            ap.error("--shape applies to --mode traffic only")
+        if args.mode not in ("traffic", "sync"):
+            ap.error("--shape applies to --mode traffic and --mode sync only")
         B_, H_, n_, d_ = (int(x) for x in args.shape.split(","))
         w = inputgen.Workload(f"shape_{B_}x{H_}x{n_}x{d_}", B_, H_, n_, d_, "bf16", seed=w.seed)
     t = inputgen.draw(w.B, w.H, w.n, w.d, w.dtype, seed=w.seed, with_do=True)
@@ -581,6 +645,16 @@ def main():
         mea.attn_bwd(q, k, v, o, do, m, l, dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream)
         if ev is not None:
             ev[2].record(stream)
+
+    if args.mode == "sync":
+        r = run_sync(step, (o, m, l, dq, dk, dv), args.steps, dev)
+        r["config"] = {"workload": w.name, "B": w.B, "H": w.H, "n": w.n, "d": w.d, "dtype": w.dtype}
+        for name, x in r["loops"].items():
+            log(f"{name}: {x['loop_cycles_per_tile']:.0f} cycles per tile per wave; copy wait "
+                f"{x['copy_wait_cycles_per_tile']:.0f} ({100 * x['copy_wait_share']:.1f}%), "
+                f"barrier {x['barrier_cycles_per_tile']:.0f} ({100 * x['barrier_share']:.1f}%)")
+        print(json.dumps(r), flush=True)
+        return
 
     # Warm-up: at least --warmup steps and at least MIN_BENCH_WARM_S of wall time, so
     # the timed steps start on a chip that has left its idle clock (the timed step

@@ -8,6 +8,7 @@ arithmetic runs in the library's HIP kernels; there is no fallback path, and
 every function raises if the library has not been built.
 """
 
+import contextlib
 import ctypes
 import os
 
@@ -16,7 +17,7 @@ __all__ = [
     "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str", "mea_version",
     "attn_fwd_ex", "attn_bwd_ex", "attn_bwd_ex_workspace_bytes",
     "attn_fwd_splitkv", "attn_fwd_splitkv_num_splits", "attn_fwd_splitkv_workspace_bytes",
-    "attn_bwd_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "attn_bwd_noalloc", "NOALLOC_SCRATCH_BYTES", "load", "using", "timing_library_path",
 ]
 
 DTYPE_F32 = 0
@@ -35,6 +36,11 @@ def library_path():
     return os.path.join(_HERE, "libmea.so")
 
 
+def timing_library_path():
+    """The timing build (same kernels, plus end-of-tile cycle counters)."""
+    return os.path.join(_HERE, "libmea_synctimers.so")
+
+
 class MeaError(RuntimeError):
     """A non-OK status returned by the library."""
 
@@ -46,9 +52,27 @@ class MeaError(RuntimeError):
 def lib():
     """The loaded ``libmea.so`` (ctypes.CDLL), with argument types declared."""
     global _LIB
-    if _LIB is not None:
-        return _LIB
-    path = library_path()
+    if _LIB is None:
+        _LIB = load(library_path())
+    return _LIB
+
+
+@contextlib.contextmanager
+def using(handle):
+    """Route the wrappers below through another build of the library (a handle
+    from ``load``, e.g. the timing library) inside the ``with`` block."""
+    global _LIB
+    saved = lib()
+    _LIB = handle
+    try:
+        yield handle
+    finally:
+        _LIB = saved
+
+
+def load(path):
+    """A ctypes handle on a build of the library at ``path``, with the C ABI's
+    argument types declared."""
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it with `python -m memory_efficient_exact_amd.build` "
@@ -80,7 +104,6 @@ def lib():
     L.attn_status_str.restype = ctypes.c_char_p
     L.mea_version.argtypes = []
     L.mea_version.restype = i32
-    _LIB = L
     return L
 
 

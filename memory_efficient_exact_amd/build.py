@@ -5,7 +5,10 @@ Usage: ``python -m memory_efficient_exact_amd.build [-v]``. Each source under
 ``csrc/`` is compiled to an object in ``_build/`` (in parallel), then linked
 into ``memory_efficient_exact_amd/libmea.so`` atomically; ``probes/mea_probe.hip``
 becomes the executable ``probes/mea_probe`` (run by ``bench.py --mode probe``).
-Always recompiles.
+The same sources built with ``MEA_SYNC_TIMERS=1`` give
+``memory_efficient_exact_amd/libmea_synctimers.so``, the timing library that
+counts the cycles of the tiled loops' end-of-tile waits (``bench.py --mode
+sync``); nothing else loads it. Always recompiles.
 """
 
 import concurrent.futures
@@ -17,6 +20,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(os.path.dirname(PKG), "_build")
 LIB = os.path.join(PKG, "libmea.so")
+SYNC_LIB = os.path.join(PKG, "libmea_synctimers.so")
 PROBE_SRC = os.path.join(PKG, "probes", "mea_probe.hip")
 PROBE = os.path.join(PKG, "probes", "mea_probe")
 ARCH = os.environ.get("MEA_OFFLOAD_ARCH", "gfx950")
@@ -54,18 +58,23 @@ def _run(cmd, verbose):
 
 
 def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
+    sync_dir = os.path.join(BUILD, "synctimers")
+    os.makedirs(sync_dir, exist_ok=True)
     srcs = sources()
     objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    sync_objs = [os.path.join(sync_dir, os.path.basename(s)[:-4] + ".o") for s in srcs]
     probe_tmp = PROBE + ".tmp"
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
         futs = [ex.submit(_run, [HIPCC, *FLAGS, "-c", s, "-o", o], verbose) for s, o in zip(srcs, objs)]
+        futs += [ex.submit(_run, [HIPCC, *FLAGS, "-DMEA_SYNC_TIMERS=1", "-c", s, "-o", o], verbose)
+                 for s, o in zip(srcs, sync_objs)]
         futs.append(ex.submit(_run, [HIPCC, *FLAGS, PROBE_SRC, "-o", probe_tmp], verbose))
         for f in futs:
             f.result()
-    tmp = LIB + ".tmp"
-    _run([HIPCC, *FLAGS, "-shared", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
+    for out, parts in ((LIB, objs), (SYNC_LIB, sync_objs)):
+        tmp = out + ".tmp"
+        _run([HIPCC, *FLAGS, "-shared", "-o", tmp, *parts], verbose)
+        os.replace(tmp, out)
     os.replace(probe_tmp, PROBE)
     return LIB
 

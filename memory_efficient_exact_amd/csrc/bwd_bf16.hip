@@ -53,6 +53,15 @@
 namespace mea {
 namespace {
 
+#if MEA_SYNC_TIMERS
+// per role: {copy wait, barrier, loop cycles, tiles, waves}; roles: d = 64 dK/dV,
+// d = 64 dQ, d = 128 dK/dV, d = 128 dQ
+__device__ unsigned long long g_sync[4][5];
+#define MEA_SYNC_COUNTERS(role) (g_sync[role])
+#else
+#define MEA_SYNC_COUNTERS(role) nullptr
+#endif
+
 constexpr int kThreads = 256;     // row-term kernel
 constexpr int kWaves = 4;         // waves per main-kernel workgroup on small grids
 constexpr int kWideWaves = 8;     // waves per main-kernel workgroup on grids that fill the chip
@@ -240,24 +249,26 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int wg, bf16* s0, bf
   // this workgroup's query tiles [t0, t1): all of them unless the backward is split
   const int t0 = sp * a.len_q;
   const int t1 = min(t0 + a.len_q, (n_q + kTileQ - 1) / kTileQ);
+  SyncTimer tim;
   auto step = [&](const bf16* qs, const bf16* os, const float* fs, bf16* qn, bf16* on, float* fn,
                   int t) {
     const int i0 = t * kTileQ;
     if (t + 1 < t1) issue(qn, on, fn, i0 + kTileQ);
     if (i0 + kTileQ <= n_q) tile_body(qs, os, fs, i0, std::false_type{});
     else tile_body(qs, os, fs, i0, std::true_type{});
-    wait_all();
-    __syncthreads();
+    tim.end_of_tile();
   };
   if (t1 > t0) {  // no query rows at all: dK = dV = 0
     issue(s0, s1, f0, t0 * kTileQ);
     wait_all();
     __syncthreads();
   }
+  tim.start();
   for (int t = t0; t < t1; t += 2) {
     step(s0, s1, f0, s2, s3, f1, t);
     if (t + 1 < t1) step(s2, s3, f1, s0, s1, f0, t + 1);
   }
+  tim.flush(MEA_SYNC_COUNTERS(0), lane);
 
   if (a.Pdk != nullptr) {  // split: this range's fp32 partials, dK before its factor
     if (key < n_k) {
@@ -384,6 +395,7 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int wg, bf16* s0, bf16
   // this workgroup's key tiles [t0, t1): all of them unless the backward is split
   const int t0 = sp * a.len_k;
   const int t1 = min(t0 + a.len_k, (n_k + kTileK - 1) / kTileK);
+  SyncTimer tim;
   auto step = [&](const bf16* ks, const bf16* vs, bf16* kn, bf16* vn, int t) {
     const int j0 = t * kTileK;
     if (t + 1 < t1) {
@@ -392,17 +404,18 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int wg, bf16* s0, bf16
     }
     if (j0 + kTileK <= n_k) tile_body(ks, vs, j0, std::false_type{});
     else tile_body(ks, vs, j0, std::true_type{});
-    wait_all();
-    __syncthreads();
+    tim.end_of_tile();
   };
   dma.issue(a.K + kbase, t0 * kTileK, n_k, s0);
   dma.issue(a.V + kbase, t0 * kTileK, n_k, s1);
   wait_all();
   __syncthreads();
+  tim.start();
   for (int t = t0; t < t1; t += 2) {
     step(s0, s1, s2, s3, t);
     if (t + 1 < t1) step(s2, s3, s0, s1, t + 1);
   }
+  tim.flush(MEA_SYNC_COUNTERS(1), lane);
 
   if (a.Pdq != nullptr) {  // split: this range's fp32 partial, before the 1/sqrt(d) factor
     if (row < n_q) {
@@ -622,24 +635,26 @@ __device__ __forceinline__ void dkdv_role128(const BwdArgs& a, int wg, bf16* s0,
   // this workgroup's query tiles [t0, t1): all of them unless the backward is split
   const int t0 = sp * a.len_q;
   const int t1 = min(t0 + a.len_q, (n_q + kTileQ - 1) / kTileQ);
+  SyncTimer tim;
   auto step = [&](const bf16* qs, const bf16* os, const float* fs, bf16* qn, bf16* on, float* fn,
                   int t) {
     const int i0 = t * kTileQ;
     if (t + 1 < t1) issue(qn, on, fn, i0 + kTileQ);
     if (i0 + kTileQ <= n_q) tile_body(qs, os, fs, i0, std::false_type{});
     else tile_body(qs, os, fs, i0, std::true_type{});
-    wait_all();
-    __syncthreads();
+    tim.end_of_tile();
   };
   if (t1 > t0) {  // no query rows at all: dK = dV = 0
     issue(s0, s1, f0, t0 * kTileQ);
     wait_all();
     __syncthreads();
   }
+  tim.start();
   for (int t = t0; t < t1; t += 2) {
     step(s0, s1, f0, s2, s3, f1, t);
     if (t + 1 < t1) step(s2, s3, f1, s0, s1, f0, t + 1);
   }
+  tim.flush(MEA_SYNC_COUNTERS(2), lane);
 
   if (a.Pdk != nullptr) {  // split: this range's fp32 partials, dK before its factor
     if (key < n_k) {
@@ -750,6 +765,7 @@ __device__ __forceinline__ void dq_role128(const BwdArgs& a, int wg, bf16* s0, b
   // this workgroup's key tiles [t0, t1): all of them unless the backward is split
   const int t0 = sp * a.len_k;
   const int t1 = min(t0 + a.len_k, (n_k + kTileK - 1) / kTileK);
+  SyncTimer tim;
   auto step = [&](const bf16* ks, const bf16* vs, bf16* kn, bf16* vn, int t) {
     const int j0 = t * kTileK;
     if (t + 1 < t1) {
@@ -758,17 +774,18 @@ __device__ __forceinline__ void dq_role128(const BwdArgs& a, int wg, bf16* s0, b
     }
     if (j0 + kTileK <= n_k) tile_body(ks, vs, j0, std::false_type{});
     else tile_body(ks, vs, j0, std::true_type{});
-    wait_all();
-    __syncthreads();
+    tim.end_of_tile();
   };
   dma.issue(a.K + kbase, t0 * kTileK, n_k, s0);
   dma.issue(a.V + kbase, t0 * kTileK, n_k, s1);
   wait_all();
   __syncthreads();
+  tim.start();
   for (int t = t0; t < t1; t += 2) {
     step(s0, s1, s2, s3, t);
     if (t + 1 < t1) step(s2, s3, s0, s1, t + 1);
   }
+  tim.flush(MEA_SYNC_COUNTERS(3), lane);
 
   if (a.Pdq != nullptr) {  // split: this range's fp32 partial, before the 1/sqrt(d) factor
     if (row < n_q) {
@@ -914,3 +931,20 @@ hipError_t launch_bwd_bf16(int d, const BwdProblem& p, hipStream_t stream) {
 }
 
 }  // namespace mea
+
+#if MEA_SYNC_TIMERS
+// Timing library only: copies the backward's 4 x 5 synchronisation counters to
+// `out` (host memory) after a device synchronisation, and clears them if
+// `reset`. Returns 0 or the failing hipError_t.
+extern "C" __attribute__((visibility("default"))) int mea_sync_timers_bwd(unsigned long long* out,
+                                                                        int reset) {
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpyFromSymbol(out, HIP_SYMBOL(mea::g_sync), sizeof(mea::g_sync));
+  if (e == hipSuccess && reset) {
+    const unsigned long long zero[4][5] = {};
+    e = hipMemcpyToSymbol(HIP_SYMBOL(mea::g_sync), zero, sizeof(zero));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+  }
+  return (int)e;
+}
+#endif

@@ -61,6 +61,15 @@
 namespace mea {
 namespace {
 
+#if MEA_SYNC_TIMERS
+// {copy wait, barrier, loop cycles, tiles, waves} of the row-tiled layout and of
+// the decoding layout
+__device__ unsigned long long g_sync[2][5];
+#define MEA_SYNC_COUNTERS(layout) (g_sync[layout])
+#else
+#define MEA_SYNC_COUNTERS(layout) nullptr
+#endif
+
 constexpr int kWaves = 4;       // waves per workgroup: decoding and small grids
 constexpr int kWideWaves = 8;   // waves per workgroup when the grid fills the chip
 constexpr float kRefSlack = 8.0f;  // log2 units a row max may exceed its reference
@@ -276,6 +285,7 @@ __global__ __launch_bounds__(64 * W, (kDecode && D == 128) ? 1 : 2) void fwd_bf1
 
   const int ntiles = (n + BC - 1) / BC;
   // one tile: prefetch the next tile into (kn, vn) while computing on (ks, vs)
+  SyncTimer tim;
   auto step = [&](const bf16* ks, const bf16* vs, bf16* kn, bf16* vn, int t) {
     const int j0 = t * BC;
     if (t + 1 < ntiles) issue(kn, vn, j0 + BC);
@@ -284,7 +294,7 @@ __global__ __launch_bounds__(64 * W, (kDecode && D == 128) ? 1 : 2) void fwd_bf1
       else if (j0 + wave * 32 < n) block(ks, vs, wave, j0, std::true_type{});
     } else if (j0 + BC <= n) {
       // two 32-key blocks per loop pass: 1-3% faster than one (d = 128: 3%) with
-      // identical results; all four spill 20 bytes at d = 64
+      // identical results (unrolling all four spills 20 bytes at d = 64)
 #pragma unroll 2
       for (int sb = 0; sb < SB; ++sb) block(ks, vs, sb, j0, std::false_type{});
     } else {  // ragged last tile
@@ -293,16 +303,17 @@ __global__ __launch_bounds__(64 * W, (kDecode && D == 128) ? 1 : 2) void fwd_bf1
         block(ks, vs, sb, j0, std::true_type{});
       }
     }
-    wait_all();
-    __syncthreads();
+    tim.end_of_tile();
   };
   issue(sK0, sV0, 0);
   wait_all();
   __syncthreads();
+  tim.start();
   for (int t = 0; t < ntiles; t += 2) {
     step(sK0, sV0, sK1, sV1, t);
     if (t + 1 < ntiles) step(sK1, sV1, sK0, sV0, t + 1);
   }
+  tim.flush(MEA_SYNC_COUNTERS(kDecode ? 1 : 0), lane);
 
   if constexpr (kDecode) {
     // Merge the four waves' partial results (same 32 query rows, different
@@ -506,3 +517,20 @@ hipError_t launch_fwd_bf16(int d, const FwdProblem& p, hipStream_t stream) {
 }
 
 }  // namespace mea
+
+#if MEA_SYNC_TIMERS
+// Timing library only: copies the forward's 2 x 5 synchronisation counters to
+// `out` (host memory) after a device synchronisation, and clears them if
+// `reset`. Returns 0 or the failing hipError_t.
+extern "C" __attribute__((visibility("default"))) int mea_sync_timers_fwd(unsigned long long* out,
+                                                                        int reset) {
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpyFromSymbol(out, HIP_SYMBOL(mea::g_sync), sizeof(mea::g_sync));
+  if (e == hipSuccess && reset) {
+    const unsigned long long zero[2][5] = {};
+    e = hipMemcpyToSymbol(HIP_SYMBOL(mea::g_sync), zero, sizeof(zero));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+  }
+  return (int)e;
+}
+#endif

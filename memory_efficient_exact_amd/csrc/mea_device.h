@@ -222,6 +222,59 @@ struct TileDma {
 // wait for every outstanding memory operation of this wave
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
+// End of a staged tile in the tiled loops: every wave waits for its own tile
+// copies (wait_all) and then for the other waves (barrier), after which the next
+// tile is visible to all and the buffer just read may be refilled. Built with
+// MEA_SYNC_TIMERS=1 (the separate timing library, never libmea.so) a SyncTimer
+// also counts, per wave, the core cycles (s_memtime) spent in the copy wait and
+// in the barrier and the cycles of the whole tile loop, and flush() adds them
+// to five device counters {copy wait, barrier, loop, tiles, waves}. Without it
+// end_of_tile() is exactly wait_all() and the barrier, and the rest is empty.
+#ifndef MEA_SYNC_TIMERS
+#define MEA_SYNC_TIMERS 0
+#endif
+struct SyncTimer {
+#if MEA_SYNC_TIMERS
+  uint64_t wait = 0, bar = 0, t0 = 0;
+  uint32_t tiles = 0;
+#endif
+  __device__ __forceinline__ void start() {
+#if MEA_SYNC_TIMERS
+    t0 = __builtin_amdgcn_s_memtime();
+#endif
+  }
+  __device__ __forceinline__ void end_of_tile() {
+#if MEA_SYNC_TIMERS
+    const uint64_t ta = __builtin_amdgcn_s_memtime();
+    wait_all();
+    const uint64_t tb = __builtin_amdgcn_s_memtime();
+    __syncthreads();
+    const uint64_t tc = __builtin_amdgcn_s_memtime();
+    wait += tb - ta;
+    bar += tc - tb;
+    ++tiles;
+#else
+    wait_all();
+    __syncthreads();
+#endif
+  }
+  __device__ __forceinline__ void flush(unsigned long long* counters, int lane) {
+#if MEA_SYNC_TIMERS
+    const uint64_t loop = __builtin_amdgcn_s_memtime() - t0;
+    if (lane == 0) {
+      atomicAdd(counters + 0, (unsigned long long)wait);
+      atomicAdd(counters + 1, (unsigned long long)bar);
+      atomicAdd(counters + 2, (unsigned long long)loop);
+      atomicAdd(counters + 3, (unsigned long long)tiles);
+      atomicAdd(counters + 4, 1ull);
+    }
+#else
+    (void)counters;
+    (void)lane;
+#endif
+  }
+};
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Workgroup index remap. The hardware hands consecutive
