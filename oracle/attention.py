@@ -189,7 +189,7 @@ def single_query(qv, k, v):
     return vstar / sstar, m, sstar
 
 
-def naive_bwd(q, k, v, do, rows=None, cols=None, row_block=1024):
+def naive_bwd(q, k, v, do, rows=None, cols=None, row_block=1024, o=None):
     """Gradients of the scalar L = sum(O * dO) with respect to Q, K and V.
 
     The pages state only that the method stays differentiable and that the
@@ -211,11 +211,18 @@ def naive_bwd(q, k, v, do, rows=None, cols=None, row_block=1024):
     ``cols`` restricts dK, dV to those key rows (the full softmax is still
     formed for every query row that contributes; with an empty ``cols`` only
     the blocks holding requested rows are visited). Returns (dq, dk, dv).
+
+    ``o``: a forward output to form the row term from, D_i = dO_i . o_i, in
+    place of sum_j P_ij dP_ij. The two agree when ``o`` is the exact output,
+    since sum_j P_ij (dO_i . v_j) = dO_i . sum_j P_ij v_j. With a rounded
+    output (the bf16 forward's), this is the row term that a backward fed
+    that output computes.
     """
     q3, lead = _as_slices(q)
     k3, _ = _as_slices(k)
     v3, _ = _as_slices(v)
     do3, _ = _as_slices(do)
+    o3 = None if o is None else _as_slices(o)[0]
     G, n, d = q3.shape
     nk = k3.shape[1]
     ridx = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -241,7 +248,10 @@ def naive_bwd(q, k, v, do, rows=None, cols=None, row_block=1024):
             p = np.exp(s - s.max(axis=1, keepdims=True))
             p /= p.sum(axis=1, keepdims=True)
             dp = do3[g, b0:b1] @ v3[g].T
-            D = (p * dp).sum(axis=1, keepdims=True)
+            if o3 is None:
+                D = (p * dp).sum(axis=1, keepdims=True)
+            else:
+                D = (do3[g, b0:b1] * o3[g, b0:b1]).sum(axis=1, keepdims=True)
             ds = p * (dp - D)
             wr = want_row[b0:b1]
             hit = wr >= 0

@@ -277,6 +277,40 @@ def test_backward_subsets_equal_full():
     np.testing.assert_allclose(dv2, dv[:, cols], rtol=0, atol=1e-13)
 
 
+def test_backward_row_term_from_the_exact_output_is_the_default():
+    # D_i = dO_i . O_i equals sum_j P_ij dP_ij when O is the exact output
+    rng = np.random.default_rng(204)
+    q, k, v, do = (rng.standard_normal((2, 37, 16)) for _ in range(4))
+    o, _, _ = oracle.naive_fwd(q, k, v)
+    ref = oracle.naive_bwd(q, k, v, do)
+    got = oracle.naive_bwd(q, k, v, do, o=o, row_block=10)
+    for a, b in zip(got, ref):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_backward_row_term_from_a_perturbed_output_closed_form():
+    # o' = o + delta changes D by dD_i = dO_i . delta_i, hence dS by -P_ij dD_i:
+    # dQ_i moves by -dD_i (P K)_i / sqrt(d), dK_j by -sum_i dD_i P_ij q_i / sqrt(d),
+    # and dV not at all
+    rng = np.random.default_rng(205)
+    G, n, d = 2, 23, 8
+    q, k, v, do = (rng.standard_normal((G, n, d)) for _ in range(4))
+    o, _, _ = oracle.naive_fwd(q, k, v)
+    delta = 1e-3 * rng.standard_normal(o.shape)
+    dq0, dk0, dv0 = oracle.naive_bwd(q, k, v, do)
+    dq1, dk1, dv1 = oracle.naive_bwd(q, k, v, do, o=o + delta)
+    scale = 1.0 / math.sqrt(d)
+    s = np.einsum("gid,gjd->gij", q, k) * scale
+    p = np.exp(s - s.max(axis=2, keepdims=True))
+    p /= p.sum(axis=2, keepdims=True)
+    dD = (do * delta).sum(axis=2)
+    np.testing.assert_allclose(dq1 - dq0, -dD[:, :, None] * np.einsum("gij,gjd->gid", p, k) * scale,
+                               rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dk1 - dk0, -np.einsum("gi,gij,gid->gjd", dD, p, q) * scale,
+                               rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dv1, dv0, rtol=0, atol=0)
+
+
 # --------------------------------------------------------- planted mistakes
 # Each test plants a plausible bug in the oracle (CPU only) and checks that a
 # pin above detects it.
