@@ -341,13 +341,20 @@ SYNC_FWD_LAYOUTS = ("fwd row-tiled", "fwd decoding")
 SYNC_BWD_ROLES = ("bwd d=64 dK/dV", "bwd d=64 dQ", "bwd d=128 dK/dV", "bwd d=128 dQ")
 
 
+SYNC_COUNTERS = 7
+
+
 def derive_sync(fwd_counts, bwd_counts):
-    """Per tiled loop: {copy wait, barrier, loop cycles, tiles, waves} (sums over
-    waves, core cycles) -> cycles per tile and shares of the loop."""
+    """Per tiled loop: {copy wait, barrier, loop cycles, tiles, waves, pair idle,
+    pair loop} (sums over waves, core cycles; the last two over the first wave of
+    each SIMD pair of 8-wave workgroups) -> cycles per tile and shares of the
+    loop; pair_idle_share is the share of a SIMD's loop time in which both of its
+    waves sat at the barrier."""
     out = {}
+    c = SYNC_COUNTERS
     for names, counts in ((SYNC_FWD_LAYOUTS, fwd_counts), (SYNC_BWD_ROLES, bwd_counts)):
         for i, name in enumerate(names):
-            wait, bar, loop, tiles, waves = counts[5 * i:5 * i + 5]
+            wait, bar, loop, tiles, waves, pair_idle, pair_loop = counts[c * i:c * i + c]
             if tiles == 0 or loop == 0:
                 continue
             out[name] = {
@@ -356,6 +363,7 @@ def derive_sync(fwd_counts, bwd_counts):
                 "copy_wait_cycles_per_tile": wait / tiles,
                 "barrier_cycles_per_tile": bar / tiles,
                 "copy_wait_share": wait / loop, "barrier_share": bar / loop,
+                "pair_idle_share": pair_idle / pair_loop if pair_loop else None,
             }
     return out
 
@@ -376,7 +384,8 @@ def run_sync(step, outputs, calls, dev):
     for fn in ("mea_sync_timers_fwd", "mea_sync_timers_bwd"):
         getattr(T, fn).argtypes = [ctypes.POINTER(u64), ctypes.c_int]
         getattr(T, fn).restype = ctypes.c_int
-    fwd, bwd = (u64 * 10)(), (u64 * 20)()
+    fwd = (u64 * (len(SYNC_FWD_LAYOUTS) * SYNC_COUNTERS))()
+    bwd = (u64 * (len(SYNC_BWD_ROLES) * SYNC_COUNTERS))()
     with mea.using(T):
         t_warm = time.perf_counter()
         while time.perf_counter() - t_warm < MIN_BENCH_WARM_S:
@@ -650,9 +659,12 @@ def main():
         r = run_sync(step, (o, m, l, dq, dk, dv), args.steps, dev)
         r["config"] = {"workload": w.name, "B": w.B, "H": w.H, "n": w.n, "d": w.d, "dtype": w.dtype}
         for name, x in r["loops"].items():
+            pair = x["pair_idle_share"]
             log(f"{name}: {x['loop_cycles_per_tile']:.0f} cycles per tile per wave; copy wait "
                 f"{x['copy_wait_cycles_per_tile']:.0f} ({100 * x['copy_wait_share']:.1f}%), "
-                f"barrier {x['barrier_cycles_per_tile']:.0f} ({100 * x['barrier_share']:.1f}%)")
+                f"barrier {x['barrier_cycles_per_tile']:.0f} ({100 * x['barrier_share']:.1f}%)"
+                + (f"; both waves of a SIMD at the barrier {100 * pair:.1f}%" if pair is not None
+                   else ""))
         print(json.dumps(r), flush=True)
         return
 

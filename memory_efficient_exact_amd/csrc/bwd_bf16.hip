@@ -54,9 +54,9 @@ namespace mea {
 namespace {
 
 #if MEA_SYNC_TIMERS
-// per role: {copy wait, barrier, loop cycles, tiles, waves}; roles: d = 64 dK/dV,
+// per role: the SyncTimer counters (mea_device.h); roles: d = 64 dK/dV,
 // d = 64 dQ, d = 128 dK/dV, d = 128 dQ
-__device__ unsigned long long g_sync[4][5];
+__device__ unsigned long long g_sync[4][kSyncCounters];
 #define MEA_SYNC_COUNTERS(role) (g_sync[role])
 #else
 #define MEA_SYNC_COUNTERS(role) nullptr
@@ -263,7 +263,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int wg, bf16* s0, bf
     wait_all();
     __syncthreads();
   }
-  tim.start();
+  tim.start(wave, W);
   for (int t = t0; t < t1; t += 2) {
     step(s0, s1, f0, s2, s3, f1, t);
     if (t + 1 < t1) step(s2, s3, f1, s0, s1, f0, t + 1);
@@ -410,7 +410,7 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int wg, bf16* s0, bf16
   dma.issue(a.V + kbase, t0 * kTileK, n_k, s1);
   wait_all();
   __syncthreads();
-  tim.start();
+  tim.start(wave, W);
   for (int t = t0; t < t1; t += 2) {
     step(s0, s1, s2, s3, t);
     if (t + 1 < t1) step(s2, s3, s0, s1, t + 1);
@@ -649,7 +649,7 @@ __device__ __forceinline__ void dkdv_role128(const BwdArgs& a, int wg, bf16* s0,
     wait_all();
     __syncthreads();
   }
-  tim.start();
+  tim.start(wave, W);
   for (int t = t0; t < t1; t += 2) {
     step(s0, s1, f0, s2, s3, f1, t);
     if (t + 1 < t1) step(s2, s3, f1, s0, s1, f0, t + 1);
@@ -780,7 +780,7 @@ __device__ __forceinline__ void dq_role128(const BwdArgs& a, int wg, bf16* s0, b
   dma.issue(a.V + kbase, t0 * kTileK, n_k, s1);
   wait_all();
   __syncthreads();
-  tim.start();
+  tim.start(wave, W);
   for (int t = t0; t < t1; t += 2) {
     step(s0, s1, s2, s3, t);
     if (t + 1 < t1) step(s2, s3, s0, s1, t + 1);
@@ -933,7 +933,7 @@ hipError_t launch_bwd_bf16(int d, const BwdProblem& p, hipStream_t stream) {
 }  // namespace mea
 
 #if MEA_SYNC_TIMERS
-// Timing library only: copies the backward's 4 x 5 synchronisation counters to
+// Timing library only: copies the backward's 4 x 7 synchronisation counters to
 // `out` (host memory) after a device synchronisation, and clears them if
 // `reset`. Returns 0 or the failing hipError_t.
 extern "C" __attribute__((visibility("default"))) int mea_sync_timers_bwd(unsigned long long* out,
@@ -941,7 +941,7 @@ extern "C" __attribute__((visibility("default"))) int mea_sync_timers_bwd(unsign
   hipError_t e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipMemcpyFromSymbol(out, HIP_SYMBOL(mea::g_sync), sizeof(mea::g_sync));
   if (e == hipSuccess && reset) {
-    const unsigned long long zero[4][5] = {};
+    const unsigned long long zero[4][mea::kSyncCounters] = {};
     e = hipMemcpyToSymbol(HIP_SYMBOL(mea::g_sync), zero, sizeof(zero));
     if (e == hipSuccess) e = hipDeviceSynchronize();
   }

@@ -62,9 +62,9 @@ namespace mea {
 namespace {
 
 #if MEA_SYNC_TIMERS
-// {copy wait, barrier, loop cycles, tiles, waves} of the row-tiled layout and of
-// the decoding layout
-__device__ unsigned long long g_sync[2][5];
+// the SyncTimer counters (mea_device.h) of the row-tiled layout and of the
+// decoding layout
+__device__ unsigned long long g_sync[2][kSyncCounters];
 #define MEA_SYNC_COUNTERS(layout) (g_sync[layout])
 #else
 #define MEA_SYNC_COUNTERS(layout) nullptr
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(64 * W, (kDecode && D == 128) ? 1 : 2) void fwd_bf1
   issue(sK0, sV0, 0);
   wait_all();
   __syncthreads();
-  tim.start();
+  tim.start(wave, W);
   for (int t = 0; t < ntiles; t += 2) {
     step(sK0, sV0, sK1, sV1, t);
     if (t + 1 < ntiles) step(sK1, sV1, sK0, sV0, t + 1);
@@ -519,7 +519,7 @@ hipError_t launch_fwd_bf16(int d, const FwdProblem& p, hipStream_t stream) {
 }  // namespace mea
 
 #if MEA_SYNC_TIMERS
-// Timing library only: copies the forward's 2 x 5 synchronisation counters to
+// Timing library only: copies the forward's 2 x 7 synchronisation counters to
 // `out` (host memory) after a device synchronisation, and clears them if
 // `reset`. Returns 0 or the failing hipError_t.
 extern "C" __attribute__((visibility("default"))) int mea_sync_timers_fwd(unsigned long long* out,
@@ -527,7 +527,7 @@ extern "C" __attribute__((visibility("default"))) int mea_sync_timers_fwd(unsign
   hipError_t e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipMemcpyFromSymbol(out, HIP_SYMBOL(mea::g_sync), sizeof(mea::g_sync));
   if (e == hipSuccess && reset) {
-    const unsigned long long zero[2][5] = {};
+    const unsigned long long zero[2][mea::kSyncCounters] = {};
     e = hipMemcpyToSymbol(HIP_SYMBOL(mea::g_sync), zero, sizeof(zero));
     if (e == hipSuccess) e = hipDeviceSynchronize();
   }

@@ -227,20 +227,33 @@ __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 // tile is visible to all and the buffer just read may be refilled. Built with
 // MEA_SYNC_TIMERS=1 (the separate timing library, never libmea.so) a SyncTimer
 // also counts, per wave, the core cycles (s_memtime) spent in the copy wait and
-// in the barrier and the cycles of the whole tile loop, and flush() adds them
-// to five device counters {copy wait, barrier, loop, tiles, waves}. Without it
-// end_of_tile() is exactly wait_all() and the barrier, and the rest is empty.
+// in the barrier and the cycles of the whole tile loop. In 8-wave workgroups,
+// whose waves w and w + 4 share a SIMD, it also counts per tile the cycles both
+// waves of a pair spend at the barrier together (the smaller of their two
+// waits: the SIMD's idle time there), exchanged through 64 bytes of LDS.
+// flush() adds the figures to seven device counters {copy wait, barrier, loop,
+// tiles, waves, pair idle, loop cycles of the waves that count pair idle}.
+// Without the switch end_of_tile() is exactly wait_all() and the barrier, and
+// the rest is empty.
 #ifndef MEA_SYNC_TIMERS
 #define MEA_SYNC_TIMERS 0
 #endif
+constexpr int kSyncCounters = 7;
 struct SyncTimer {
 #if MEA_SYNC_TIMERS
-  uint64_t wait = 0, bar = 0, t0 = 0;
-  uint32_t tiles = 0;
+  uint64_t wait = 0, bar = 0, t0 = 0, pair_idle = 0;
+  uint32_t tiles = 0, prev_bar = 0;
+  int wave = 0, waves = 0;
 #endif
-  __device__ __forceinline__ void start() {
+  __device__ __forceinline__ void start(int wave_, int waves_) {
 #if MEA_SYNC_TIMERS
+    // wave-uniform values, kept in scalar registers
+    wave = __builtin_amdgcn_readfirstlane(wave_);
+    waves = waves_;
     t0 = __builtin_amdgcn_s_memtime();
+#else
+    (void)wave_;
+    (void)waves_;
 #endif
   }
   __device__ __forceinline__ void end_of_tile() {
@@ -252,6 +265,19 @@ struct SyncTimer {
     const uint64_t tc = __builtin_amdgcn_s_memtime();
     wait += tb - ta;
     bar += tc - tb;
+    if (waves == 8) {
+      // slot parity = tile parity: a wave writes its wait for tile t after
+      // barrier t and reads its partner's wait for tile t - 1, written before
+      // barrier t; the partner rewrites that slot only after barrier t + 1
+      __shared__ uint32_t slots[2][8];
+      const uint32_t b = (uint32_t)(tc - tb);
+      slots[tiles & 1][wave] = b;
+      if (tiles > 0 && wave < 4) {
+        const uint32_t pb = __builtin_amdgcn_readfirstlane(slots[(tiles - 1) & 1][wave + 4]);
+        pair_idle += min(prev_bar, pb);
+      }
+      prev_bar = b;
+    }
     ++tiles;
 #else
     wait_all();
@@ -267,6 +293,10 @@ struct SyncTimer {
       atomicAdd(counters + 2, (unsigned long long)loop);
       atomicAdd(counters + 3, (unsigned long long)tiles);
       atomicAdd(counters + 4, 1ull);
+      if (waves == 8 && wave < 4) {
+        atomicAdd(counters + 5, (unsigned long long)pair_idle);
+        atomicAdd(counters + 6, (unsigned long long)loop);
+      }
     }
 #else
     (void)counters;

@@ -1,6 +1,7 @@
 """The timing library (libmea_synctimers.so): the same kernels built with
 MEA_SYNC_TIMERS=1, which count per wave the core cycles of each tiled loop and
-of its end-of-tile copy wait and barrier (bench.py --mode sync).
+of its end-of-tile copy wait and barrier, and per SIMD pair of an 8-wave
+workgroup the cycles both waves sit at the barrier (bench.py --mode sync).
 
 CPU: what the library exports, and the reduction of its counters. GPU: its
 outputs equal libmea.so's bit for bit, and its tile counts match the loops."""
@@ -30,19 +31,23 @@ def test_timing_library_exports_the_c_abi_and_its_two_readers():
 
 def test_sync_counter_reduction():
     import bench
-    # forward row-tiled layout: 16 waves x 8 tiles, 1000 loop cycles per tile of
-    # which 100 copy wait and 250 barrier; decoding layout unused
-    fwd = [16 * 8 * 100, 16 * 8 * 250, 16 * 8 * 1000, 16 * 8, 16] + [0] * 5
-    # backward: only the d = 64 dQ role ran (4 waves x 3 tiles)
-    bwd = [0] * 5 + [12 * 30, 12 * 60, 12 * 600, 12, 4] + [0] * 10
+    # forward row-tiled layout: 16 waves (two 8-wave workgroups) x 8 tiles, 1000
+    # loop cycles per tile of which 100 copy wait and 250 barrier; the 8 first
+    # waves of the SIMD pairs saw both waves at the barrier 40 cycles per tile;
+    # decoding layout unused
+    fwd = [16 * 8 * 100, 16 * 8 * 250, 16 * 8 * 1000, 16 * 8, 16, 8 * 8 * 40, 8 * 8 * 1000] + [0] * 7
+    # backward: only the d = 64 dQ role ran (one 4-wave workgroup x 3 tiles: no pairs)
+    bwd = [0] * 7 + [12 * 30, 12 * 60, 12 * 600, 12, 4, 0, 0] + [0] * 14
     d = bench.derive_sync(fwd, bwd)
     assert set(d) == {"fwd row-tiled", "bwd d=64 dQ"}
     f = d["fwd row-tiled"]
     assert f["tiles_per_wave"] == 8 and f["loop_cycles_per_tile"] == 1000
     assert f["copy_wait_cycles_per_tile"] == 100 and f["barrier_cycles_per_tile"] == 250
     assert f["copy_wait_share"] == pytest.approx(0.1) and f["barrier_share"] == pytest.approx(0.25)
+    assert f["pair_idle_share"] == pytest.approx(0.04)
     q = d["bwd d=64 dQ"]
     assert q["tiles_per_wave"] == 3 and q["barrier_share"] == pytest.approx(0.1)
+    assert q["pair_idle_share"] is None
 
 
 @pytest.mark.gpu
@@ -77,6 +82,8 @@ def test_timing_library_matches_libmea_and_counts_every_tile(B, H, n, d):
         assert x["waves"] > 0 and x["tiles_per_wave"] >= 1
         assert 0 <= x["copy_wait_share"] <= 1 and 0 <= x["barrier_share"] <= 1
         assert x["copy_wait_cycles_per_tile"] + x["barrier_cycles_per_tile"] <= x["loop_cycles_per_tile"]
+        if x["pair_idle_share"] is not None:  # both waves idle only while each waits
+            assert 0 <= x["pair_idle_share"] <= x["barrier_share"] * 1.05
     if d == 64:
         # a grid that fills the chip runs the backward unsplit: every wave of both
         # roles sweeps all 64-row tiles of its head
