@@ -413,7 +413,9 @@ def run_probes():
     wave count. The mixed probes put an MFMA body and an FMA body on one SIMD (two
     waves, or interleaved in one wave): valu_hidden is the share of the VALU body's
     own time that ran under the MFMAs. The exponential mixes alternate v_exp_f32 with
-    v_add_f32 or v_fma_f32: time_vs_serial_sum is 1 when they do not overlap."""
+    v_add_f32 or v_fma_f32: time_vs_serial_sum is 1 when they do not overlap. The
+    HBM streams (2 GiB read, written, copied) give the bandwidth a plain kernel
+    reaches, against which the decoding kernels are read."""
     import subprocess
     exe = os.path.join(ROOT, "memory_efficient_exact_amd", "probes", "mea_probe")
     if not os.path.exists(exe):
@@ -486,6 +488,8 @@ def derive_probes(raw):
         out["derived"][p["probe"]] = d
     out["derived"]["atomic_dq"] = {a["mode"]: {"tb_per_s": a["tb_per_s"], "ms": a["ms"]}
                                    for a in raw["atomic_dq"]}
+    out["derived"]["hbm_stream"] = {a["mode"]: {"tb_per_s": a["tb_per_s"], "ms": a["ms"]}
+                                    for a in raw.get("hbm_stream", [])}
     return out
 
 

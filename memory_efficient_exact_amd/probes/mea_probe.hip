@@ -1,7 +1,8 @@
 // Issue-cost probes for gfx950: the measurements behind the roofline reading of
 // the attention kernels (how much MFMA work and how much VALU work one SIMD can
-// issue, alone and together, and what fp32 atomic adds in the pattern of a
-// single-pass backward sustain). Register-only loops of one instruction kind,
+// issue, alone and together, what fp32 atomic adds in the pattern of a
+// single-pass backward sustain, and what plain 16-byte streams read, write and
+// copy from and to HBM: the bandwidth the decoding kernels can reach). Register-only loops of one instruction kind,
 // timed per wave with the core-clock counter (s_memtime) and the 100 MHz
 // real-time counter (s_memrealtime), whose ratio gives the clock the loop ran
 // at. Prints one JSON object on stdout.
@@ -292,6 +293,44 @@ __global__ __launch_bounds__(512) void atomic_dq_kernel(float* __restrict__ dq) 
   }
 }
 
+// HBM streams: kStreamVecs 16-byte vectors (2 GiB) over kStreamGrid workgroups of
+// 256 threads, each thread handling kStreamPerThread vectors (kStreamVecs =
+// kStreamGrid * 256 * kStreamPerThread exactly, checked on the host), UNROLL loads
+// in flight per step. STRIDED: thread t takes vectors t + j * (grid threads);
+// otherwise workgroup b streams its own contiguous chunk of 256 * kStreamPerThread
+// vectors, thread t taking vectors t + 256 * j of it. The read stream folds what
+// it reads into one word per thread (written to `sink`), so no load is dropped.
+constexpr int kStreamGrid = 8192;
+constexpr int kStreamPerThread = 64;
+constexpr size_t kStreamVecs = (size_t)kStreamGrid * 256 * kStreamPerThread;  // 2^27
+
+template <int MODE, bool STRIDED, int UNROLL>  // MODE 0: read, 1: write, 2: copy
+__global__ __launch_bounds__(256) void stream_kernel(const uint4* __restrict__ src,
+                                                     uint4* __restrict__ dst,
+                                                     unsigned* __restrict__ sink) {
+  static_assert(kStreamPerThread % UNROLL == 0, "whole steps");
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;  // < grid threads
+  const size_t base = STRIDED ? t : (size_t)blockIdx.x * 256 * kStreamPerThread + threadIdx.x;
+  const size_t step = STRIDED ? (size_t)gridDim.x * blockDim.x : 256;
+  unsigned acc = 0;
+  for (int j = 0; j < kStreamPerThread; j += UNROLL) {
+    uint4 v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const size_t i = base + (size_t)(j + u) * step;  // < kStreamVecs
+      if constexpr (MODE == 1) v[u] = make_uint4((unsigned)i, 0u, 0u, 1u);
+      else v[u] = src[i];
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const size_t i = base + (size_t)(j + u) * step;
+      if constexpr (MODE == 0) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+      else dst[i] = v[u];
+    }
+  }
+  if constexpr (MODE == 0) sink[t] = acc;
+}
+
 #define CHECK(x)                                                                  \
   do {                                                                            \
     hipError_t e_ = (x);                                                          \
@@ -406,9 +445,54 @@ int main() {
              mode ? ", " : "", modes[mode], best, bytes, bytes / (best * 1e-3) / 1e12, v0);
     json += buf;
   }
+  json += "], \"hbm_stream\": [";
+  CHECK(hipFree(dq));
+  {
+    const int threads = kStreamGrid * 256;
+    if ((size_t)threads * kStreamPerThread != kStreamVecs || kStreamPerThread % 4) return 4;
+    uint4 *a = nullptr, *b = nullptr;
+    unsigned* sk = nullptr;
+    const size_t bytes = kStreamVecs * sizeof(uint4);
+    CHECK(hipMalloc(&a, bytes));
+    CHECK(hipMalloc(&b, bytes));
+    CHECK(hipMalloc(&sk, (size_t)threads * sizeof(unsigned)));
+    CHECK(hipMemset(a, 1, bytes));
+    CHECK(hipMemset(b, 0, bytes));
+    struct Stream { const char* name; int mode; void (*kernel)(const uint4*, uint4*, unsigned*); };
+    const Stream streams[] = {
+        {"read_strided_x4", 0, stream_kernel<0, true, 4>},
+        {"read_blocked_x4", 0, stream_kernel<0, false, 4>},
+        {"read_blocked_x8", 0, stream_kernel<0, false, 8>},
+        {"write_blocked_x4", 1, stream_kernel<1, false, 4>},
+        {"copy_blocked_x4", 2, stream_kernel<2, false, 4>},
+    };
+    bool first_stream = true;
+    for (const Stream& st : streams) {
+      float best = 1e30f;
+      for (int rep = 0; rep < 4; ++rep) {  // the first launch warms the clock
+        CHECK(hipDeviceSynchronize());
+        CHECK(hipEventRecord(e0, 0));
+        hipLaunchKernelGGL(st.kernel, dim3(kStreamGrid), dim3(256), 0, 0, a, b, sk);
+        CHECK(hipGetLastError());
+        CHECK(hipEventRecord(e1, 0));
+        CHECK(hipEventSynchronize(e1));
+        float ms = 0.f;
+        CHECK(hipEventElapsedTime(&ms, e0, e1));
+        if (rep > 0) best = std::min(best, ms);
+      }
+      const double moved = (st.mode == 2 ? 2.0 : 1.0) * (double)bytes;  // copy: read + write
+      char buf[256];
+      snprintf(buf, sizeof buf, "%s{\"mode\": \"%s\", \"ms\": %.4f, \"bytes\": %.0f, \"tb_per_s\": %.3f}",
+               first_stream ? "" : ", ", st.name, best, moved, moved / (best * 1e-3) / 1e12);
+      json += buf;
+      first_stream = false;
+    }
+    CHECK(hipFree(a));
+    CHECK(hipFree(b));
+    CHECK(hipFree(sk));
+  }
   json += "]}";
   printf("%s\n", json.c_str());
-  CHECK(hipFree(dq));
   CHECK(hipFree(out));
   CHECK(hipFree(sink));
   return 0;

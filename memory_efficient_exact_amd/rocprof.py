@@ -395,7 +395,7 @@ def render(summary, title, commands, note=""):
 
 def render_probes(probe):
     """Markdown tables of `bench.py --mode probe` output (issue costs, overlap,
-    LDS-fed MFMA rate, fp32 atomic throughput)."""
+    LDS-fed MFMA rate, fp32 atomic throughput, HBM stream bandwidth)."""
     out = ["Issue-cost probes (`bench.py --mode probe`; per-wave core cycles from `s_memtime`, "
            "the clock from `s_memtime` over `s_memrealtime`):", "",
            "| probe | waves per SIMD | clock MHz | cycles per iteration (MFMA wave) | "
@@ -407,7 +407,7 @@ def render_probes(probe):
                    f"{p['mfma_per_iter']} | {p['valu_per_iter']} |")
     out += ["", "Derived:", "", "| probe | figures |", "|---|---|"]
     for k, v in probe["derived"].items():
-        if k == "atomic_dq":
+        if k in ("atomic_dq", "hbm_stream"):
             continue
         txt = ", ".join(f"{a} {b:.3f}" if isinstance(b, float) else f"{a} {b}" for a, b in v.items())
         out.append(f"| {k} | {txt} |")
@@ -416,6 +416,14 @@ def render_probes(probe):
             "| mode | ms | TB/s |", "|---|---|---|"]
     for a in probe["raw"]["atomic_dq"]:
         out.append(f"| {a['mode']} | {a['ms']:.3f} | {a['tb_per_s']:.2f} |")
+    if probe["raw"].get("hbm_stream"):
+        out += ["", "HBM streams (2 GiB of 16-byte vectors, 8192 workgroups of 256 threads; "
+                "strided: consecutive vectors across all threads, blocked: one contiguous "
+                "256 KiB chunk per workgroup; x4 / x8 loads in flight per thread; copy counts "
+                "read + write; best of three after one warm-up launch):", "",
+                "| stream | ms | bytes | TB/s |", "|---|---|---|---|"]
+        for a in probe["raw"]["hbm_stream"]:
+            out.append(f"| {a['mode']} | {a['ms']:.3f} | {a['bytes']:.0f} | {a['tb_per_s']:.2f} |")
     out.append("")
     return "\n".join(out)
 

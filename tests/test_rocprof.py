@@ -143,8 +143,13 @@ def test_probe_derivation_uses_the_register_only_mfma_time():
         _probe("v_exp_f32+v_add_f32", 1, 0.0, 56.0, 0, 8),
         _probe("one_wave:4mfma+8fma", 1, 135.0, 0.0, 4, 8),
         _probe("mfma_wave+exp_wave", 2, 160.0, 108.0, 4, 8),
-    ], "atomic_dq": [{"mode": "atomic_add_f32", "ms": 4.0, "tb_per_s": 1.07}]}
+    ], "atomic_dq": [{"mode": "atomic_add_f32", "ms": 4.0, "tb_per_s": 1.07}],
+       "hbm_stream": [{"mode": "read_blocked_x4", "ms": 0.35, "bytes": 2147483648, "tb_per_s": 6.14}]}
     d = bench.derive_probes(raw)["derived"]
+    assert d["hbm_stream"] == {"read_blocked_x4": {"tb_per_s": 6.14, "ms": 0.35}}
+    from memory_efficient_exact_amd import rocprof
+    md = rocprof.render_probes({"raw": raw, "derived": d})
+    assert "| read_blocked_x4 | 0.350 | 2147483648 | 6.14 |" in md
     assert d["mfma_32x32x16_bf16 w1"]["simd_cycles_per_mfma"] == 32.0
     assert d["v_fma_f32 w1"]["wave_cycles_per_instr"] == 5.5
     assert d["v_fma_f32 w1"]["cost_vs_v_add_f32"] == 1.1
