@@ -167,7 +167,7 @@ MEA_API mea_status_t attn_bwd(mea_dtype_t dt, int64_t B, int64_t H, int64_t n, i
  * The scratch array holds MEA_NOALLOC_SCRATCH_BYTES (32 MiB). Each GPU the
  * library runs on holds its own copy from the moment the library is loaded
  * until the process ends; its device address is looked up on the first call
- * made with that GPU current. The call needs the row terms of attn_bwd's
+ * made with that GPU current, which may itself be under HIP graph capture. The call needs the row terms of attn_bwd's
  * workspace (8*B*H*n bytes for bf16, 16*B*H*n for fp32); larger shapes are
  * rejected with MEA_ERR_WORKSPACE before anything runs. When the split layout
  * of a small grid (see attn_bwd_workspace_bytes) also fits, it is used, and

@@ -1,5 +1,6 @@
 """attn_bwd_noalloc (the backward for callers that cannot allocate) against
-attn_bwd, through the C ABI, on two calls in a row with the second smaller.
+attn_bwd, through the C ABI, on two calls in a row with the second smaller,
+and captured in a HIP graph (its first call in the process) and replayed.
 
 attn_bwd_noalloc runs in the library's per-GPU scratch array instead of a
 caller workspace. The split layout of a small grid (at most about 25 MiB)
@@ -52,6 +53,50 @@ def check_oracle(t, got, dtype):
         err = np.abs(f(g.cpu()) - r).max()
         say(name, f"max abs err vs oracle {err:.3e}")
         assert err <= TOL[dtype], (name, err)
+
+
+def test_noalloc_first_call_inside_graph_capture():
+    # The callers this entry point is for capture it in HIP graphs. Defined first in
+    # the last test file, this test makes the process's first attn_bwd_noalloc call
+    # inside a capture (that call also looks up the scratch array's device address);
+    # nothing runs it earlier. A small grid, so the split layout runs in the array.
+    # Every replay, with new inputs copied in and eager work between replays, must
+    # equal the eager attn_bwd given its workspace, bit for bit.
+    say("noalloc captured in a graph")
+    shape = (1, 2, 1000, 64)
+    B, H, n, d = shape
+    q, k, v, do, o = (torch.empty(shape, dtype=torch.bfloat16, device=DEV) for _ in range(5))
+    m = torch.empty(shape[:3], device=DEV)
+    l = torch.empty_like(m)
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(mea.attn_bwd_workspace_bytes(mea.DTYPE_BF16, B, H, n, d), dtype=torch.uint8,
+                     device=DEV)
+
+    def load(seed):
+        t = inputgen.draw(*shape, "bf16", seed=seed, with_do=True)
+        for buf, name in zip((q, k, v, do), ("q", "k", "v", "do")):
+            buf.copy_(t[name])
+        mea.attn_fwd(q, k, v, out=o, row_max=m, row_sum=l)
+        torch.cuda.synchronize()
+        return t
+
+    load(150)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            mea.attn_bwd_noalloc(q, k, v, o, do, m, l, *grads)
+    torch.cuda.synchronize()
+    for replay, seed in enumerate((151, 152, 153)):
+        t = load(seed)
+        g.replay()
+        torch.cuda.synchronize()
+        ref = mea.attn_bwd(q, k, v, o, do, m, l, workspace=ws)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dQ", "dK", "dV"), grads, ref):
+            assert torch.equal(a, b), (replay, name)
+    check_oracle(t, grads, "bf16")
 
 
 @pytest.mark.parametrize("dtype,d,first,second", [
