@@ -214,12 +214,14 @@ __global__ __launch_bounds__(64 * W, (kDecode && D == 128) ? 1 : 2) void fwd_bf1
       v_off[db][h] = L::off(4 * hi + (jj >> 2) + 8 * h, db * 32 + (g & 1) * 16 + 4 * (jj & 3));
 
   // The softmax of a block (masking, maxima, rescale, exponentials) runs at raised
-  // issue priority in the d = 64 8-wave layout: the wave that enters it wins VALU
-  // issue over the other wave of its SIMD, whose MFMAs keep the matrix pipe busy
-  // meanwhile. 4% faster at 1 x 16 x 16384 x 64 and 2 x 8 x 8192 x 64 with identical
-  // results; neutral at d = 128 and 2-3% slower in the decoding layout, which keep
-  // the default priority. (Raising the MFMA phases instead changed nothing.)
-  constexpr bool kSoftmaxPrio = D == 64 && W == 8 && !kDecode;
+  // issue priority in the d = 64 row-tiled layouts: the wave that enters it wins
+  // VALU issue over the other wave of its SIMD, whose MFMAs keep the matrix pipe
+  // busy meanwhile. With identical results, 4% faster at 1 x 16 x 16384 x 64 and
+  // 2 x 8 x 8192 x 64 (8-wave workgroups) and 3.6-5.5% on 4-wave grids of two
+  // workgroups per CU (1 x 24 x 4096 x 64); neutral at d = 128 and 2-3% slower in the
+  // decoding layout, which keep the default priority. (Raising the MFMA phases
+  // instead changed nothing.)
+  constexpr bool kSoftmaxPrio = D == 64 && !kDecode;
 
   // One 32-key block: scores, online softmax, P V.
   auto block = [&](const bf16* ks, const bf16* vs, int sb, int j0, auto masked_tag) {
