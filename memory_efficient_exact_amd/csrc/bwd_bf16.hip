@@ -743,6 +743,12 @@ __device__ __forceinline__ void dq_role128(const BwdArgs& a, int wg, bf16* s0, b
           s = mfma16x16x32(lds_read_b128(ks + off), qf[dk], s);
           dp = mfma16x16x32(lds_read_b128(vs + off), of[dk], dp);
         }
+        // the exponentials and dS of a block at raised issue priority in 8-wave
+        // workgroups: the wave in them wins VALU issue over the other wave of its
+        // SIMD, whose MFMAs keep the matrix pipe busy meanwhile (1% faster at
+        // 1 x 16 x 8192 x 128 and 2 x 32 x 2048 x 128 with identical results; 1%
+        // slower with 4-wave workgroups; the dK/dV role spills with it)
+        if constexpr (W == 8) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float p = fast_exp2(__builtin_fmaf(s[r], a.C, -lse));
@@ -751,6 +757,7 @@ __device__ __forceinline__ void dq_role128(const BwdArgs& a, int wg, bf16* s0, b
           }
           sf[4 * h + r] = (bf16)(p * dp[r]);
         }
+        if constexpr (W == 8) __builtin_amdgcn_s_setprio(0);
       }
       // dQ^T += K^T dS^T over the 32 keys of chunk c
 #pragma unroll
