@@ -31,6 +31,7 @@ import statistics
 
 XCDS = 8
 SIMDS = 1024
+CUS = 256
 
 # one rocprofv3 run per pass: the hardware collects these counter sets together
 PASSES = {
@@ -189,6 +190,9 @@ def derive(c):
             out["mfma_busy"] = g("SQ_VALU_MFMA_BUSY_CYCLES") / (SIMDS * cyc)
         if g("SQ_VALU_MFMA_COEXEC_CYCLES") is not None:
             out["mfma_valu_coissue"] = g("SQ_VALU_MFMA_COEXEC_CYCLES") / (SIMDS * cyc)
+        if g("SQ_LDS_IDX_ACTIVE") is not None:
+            # share of cycles each CU's LDS spends on indexed (ds_*) operations
+            out["lds_busy"] = g("SQ_LDS_IDX_ACTIVE") / (CUS * cyc)
     if g("SQ_INSTS_MFMA"):
         out["mfma_insts"] = g("SQ_INSTS_MFMA")
         if g("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
@@ -360,19 +364,19 @@ def render(summary, title, commands, note=""):
         out += ["Counters (mean per dispatch):", "",
                 "| kernel | cycles per XCD | MFMA instr. | busy cycles / MFMA | MFMA busy | "
                 "MFMA+VALU co-issue | wave time in VALU | VALU instr. | `v_exp_f32` | wave time waiting | "
-                "waiting to issue | LDS instr. | LDS / MFMA | LDS bank-conflict cycles |",
-                "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+                "waiting to issue | LDS instr. | LDS / MFMA | LDS busy | LDS bank-conflict cycles |",
+                "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
         for e in ks.values():
             if "mfma_busy" not in e and "wait_any_share" not in e:
                 continue
-            out.append("| `{}` | {} | {} | {} | {} | {} | {} | {} | {} | {} | {} | {} | {} | {} |".format(
+            out.append("| `{}` | {} | {} | {} | {} | {} | {} | {} | {} | {} | {} | {} | {} | {} | {} |".format(
                 e["kernel"], _fmt(e.get("cycles_per_xcd"), "sci"), _fmt(e.get("mfma_insts"), "sci"),
                 _fmt(e.get("busy_cycles_per_mfma"), "f1"), _fmt(e.get("mfma_busy"), "pct"),
                 _fmt(e.get("mfma_valu_coissue"), "pct"), _fmt(e.get("valu_share"), "pct"),
                 _fmt(e.get("valu_insts"), "sci"), _fmt(e.get("exp_f32_insts"), "sci"),
                 _fmt(e.get("wait_any_share"), "pct"), _fmt(e.get("wait_issue_share"), "pct"),
                 _fmt(e.get("lds_insts"), "sci"), _fmt(e.get("lds_insts_per_mfma"), "f2"),
-                _fmt(e.get("lds_bank_conflict_cycles"), "sci")))
+                _fmt(e.get("lds_busy"), "pct"), _fmt(e.get("lds_bank_conflict_cycles"), "sci")))
         out.append("")
     if summary.get("read_factor") is not None or summary.get("write_factor") is not None:
         out += [f"HBM traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by the "

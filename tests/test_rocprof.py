@@ -46,7 +46,9 @@ def prof(tmp_path):
                                   "SQ_WAVE_CYCLES": 1e9, "SQ_ACTIVE_INST_VALU": 2.5e8})
     write_csv(str(d / "pmcA" / "run_counter_collection.csv"), rows)
     # pass B: per-instance rows of one counter are summed per dispatch
-    rows = counter_rows(BWD, 1, {"SQ_WAVE_CYCLES": 1e9, "SQ_WAIT_ANY": 4e8, "SQ_INSTS_LDS": 3.2e7})
+    # SQ_LDS_IDX_ACTIVE 6.4e7 = a quarter of 256 CUs x 1e6 cycles (the cycles of pass A)
+    rows = counter_rows(BWD, 1, {"SQ_WAVE_CYCLES": 1e9, "SQ_WAIT_ANY": 4e8, "SQ_INSTS_LDS": 3.2e7,
+                                 "SQ_LDS_IDX_ACTIVE": 6.4e7})
     rows += counter_rows(BWD, 1, {"SQ_LDS_BANK_CONFLICT": 1e6})
     rows += counter_rows(BWD, 1, {"SQ_LDS_BANK_CONFLICT": 2e6})
     write_csv(str(d / "pmcB" / "run_counter_collection.csv"), rows)
@@ -80,6 +82,7 @@ def test_collect_and_derive(prof):
     assert e["wait_any_share"] == pytest.approx(0.4)
     assert e["lds_insts_per_mfma"] == pytest.approx(2.0)
     assert e["lds_bank_conflict_cycles"] == pytest.approx(3e6)
+    assert e["lds_busy"] == pytest.approx(0.25)
     assert e["hbm_read_bytes"] == pytest.approx(2 * 1024 * 1024)
     assert e["hbm_write_bytes"] == pytest.approx(512 * 1024)
     assert e["hbm_gbs"] == pytest.approx(2.5 * 2 ** 20 / 2.5e-3 / 1e9)
