@@ -7,6 +7,9 @@ cross-compiles for gfx950; nothing here runs on a GPU).
    for the reads a use needs (lgkmcnt(n), LDS reads return in issue order).
 2. The d = 64 backward issues its tile copies from inline assembly, out of the
    pass's sight, so its LDS reads keep those partial waits.
+3. The tiled loops of the hot kernels do not copy their running state between
+   register sets at every tile (they did while the full and the masked tile
+   paths met inside the loop: 16-40 moves per block).
 """
 
 import os
@@ -100,3 +103,34 @@ def test_d128_backward_dq_role_keeps_partial_lds_waits(tmp_path):
     full, partial = lds_waits(function_body(asm, r"_ZN3mea12_GLOBAL__N_118bwd_main128_kernelILi8EEEv\w*"))
     # all 221 were full with the builtin copies in both roles
     assert partial >= 40, (full, partial)
+
+
+def loop_blocks(body):
+    """{label: (loop annotation, number of v_mov instructions)} of the basic blocks."""
+    blocks, cur = {}, None
+    for line in body.split("\n"):
+        t = line.strip()
+        m = re.match(r"^(\.LBB\S+|; %bb\.\d+):\s*(.*)$", t)
+        if m:
+            cur = m.group(1)
+            blocks[cur] = [m.group(2), 0]
+        elif cur and t.startswith("v_mov"):
+            blocks[cur][1] += 1
+    return blocks
+
+
+@pytest.mark.parametrize("src,symbol", [
+    ("fwd_bf16.hip", r"_ZN3mea12_GLOBAL__N_115fwd_bf16_kernelILi64ELi2ELi128ELb0ELi8EEEv\w*"),
+    ("fwd_bf16.hip", r"_ZN3mea12_GLOBAL__N_115fwd_bf16_kernelILi128ELi1ELi64ELb0ELi8EEEv\w*"),
+    ("bwd_bf16.hip", r"_ZN3mea12_GLOBAL__N_115bwd_main_kernelILi64ELi8EEEv\w*"),
+    ("bwd_bf16.hip", r"_ZN3mea12_GLOBAL__N_118bwd_main128_kernelILi8EEEv\w*"),
+])
+def test_tile_loops_do_not_copy_their_running_state(tmp_path, src, symbol):
+    # With the ragged last tile handled outside the tiled loops, no block inside a loop
+    # moves the accumulators between register sets (a block of 16-80 v_mov per tile
+    # when a full and a masked tile path met inside the loop).
+    asm = assemble(os.path.join(ROOT, "memory_efficient_exact_amd", "csrc", src),
+                   str(tmp_path / "k.s"))
+    body = function_body(asm, symbol)
+    copies = {b: n for b, (note, n) in loop_blocks(body).items() if "Loop" in note and n >= 12}
+    assert not copies, copies
