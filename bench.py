@@ -501,6 +501,7 @@ def profile_tools(args):
     program = _traffic_program(args.shape, args.pmc_mode)
     kt = "python3 " + os.path.join(ROOT, "bench.py") + (
         f" --mode {args.kt_mode}" if args.kt_mode else "") + (
+        f" --shape {args.shape}" if args.kt_mode and args.shape else "") + (
         " --no-cpu-baseline" if args.no_cpu_baseline else "")
     cmds = rocprof.plan(os.path.abspath(args.prof_dir), program,
                         kt_program=kt if (args.kt_mode or not args.shape) else None)
