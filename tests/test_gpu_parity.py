@@ -267,6 +267,43 @@ def test_permuting_kv_pairs(dtype):
     check("O perm", f64(o2.cpu()), f64(o1.cpu()), dtype)
 
 
+# Scores that climb past the reference in every 32-key block: key j carries
+# alpha * j in column 0 and q has 1 there, so each block's row maximum exceeds
+# the previous block's by about 32 * alpha raw units (> 8 in log2 units), and
+# every block takes the rebase path (new reference, rescaled acc and l, the
+# block's weights formed again). One shape per forward layout.
+CLIMB = [
+    (1, 2, 1000, 64),    # decoding layout (small grid)
+    (1, 40, 1000, 64),   # 4-wave row-tiled layout
+    (1, 130, 1000, 64),  # 8-wave row-tiled layout
+    (1, 20, 1000, 128),  # 4-wave row-tiled layout, d = 128
+    (1, 64, 1000, 128),  # 8-wave row-tiled layout, d = 128
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("B,H,n,d,splits", [c + (1,) for c in CLIMB] + [(1, 2, 1000, 64, 4),
+                                                                         (1, 2, 1000, 128, 4)])
+def test_scores_climbing_every_block(dtype, B, H, n, d, splits):
+    say("climbing scores", dtype, B, H, n, d, "splits", splits)
+    t = inputgen.draw(B, H, n, d, "fp32", seed=11)
+    alpha = 2.5 if d == 64 else 3.5
+    q = t["q"] * 0.5
+    q[..., 0] = 1.0
+    k = t["k"].clone()
+    k[..., 0] = alpha * torch.arange(n, dtype=torch.float32)
+    cast = torch.bfloat16 if dtype == "bf16" else torch.float32
+    t = {"q": q.to(cast), "k": k.to(cast), "v": t["v"].to(cast)}
+    if splits == 1:
+        o, m, l = run_fwd(t)
+    else:  # key ranges whose maxima differ by far more than the threshold, then the merge
+        o, m, l = mea.attn_fwd_splitkv(gpu(t["q"]), gpu(t["k"]), gpu(t["v"]), num_splits=splits)
+        torch.cuda.synchronize()
+    o_ref, m_ref, l_ref = oracle_heads(oracle.naive_fwd, f64(t["q"]), f64(t["k"]), f64(t["v"]))
+    check("O", f64(o.cpu()), o_ref, dtype, tag=f"climb {dtype} {B}x{H}x{n}x{d} splits {splits}")
+    check_stats(m.cpu().numpy(), l.cpu().numpy(), m_ref, l_ref, dtype)
+
+
 def test_runs_are_bitwise_deterministic():
     say("determinism")
     t = inputgen.draw(2, 4, 1000, 64, "bf16", seed=8, with_do=True)
